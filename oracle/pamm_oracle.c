@@ -37,7 +37,8 @@
  *   R5  ties go to the lowest generator slot; a NaN score never wins.
  *   R6  f is int32 with -1 marking a dropped row (alpha = 0 there); alpha is
  *       fp32; C keeps the input dtype.
- *   R7  a generator of zero norm scores 0; a row of zero norm has cosine 0.
+ *   R7  a generator of zero norm scores 0; a row of zero norm has cosine 0;
+ *       a row containing NaN has a NaN cosine and is dropped.
  *   R8  the argmax and the epsilon test are decided on fp32 values (each fp64
  *       score rounded once to fp32), the precision of the GPU kernel; the
  *       numbers behind the decision are computed in fp64.
@@ -228,9 +229,11 @@ int orc_compress(const void *X, int64_t n, int64_t d, int64_t ldx, int dtype,
             if (s32 != s32) continue;
             if (best < 0 || s32 > best32) { best = j; best32 = s32; }
         }
+        /* cosine of the winner: 0 for a zero row (R7); a row holding NaN has
+         * a NaN norm and a NaN cosine, which never passes the eps test */
         double xn = sqrt(xn2);
         double cs = 0.0;
-        if (best >= 0) cs = xn2 > 0.0 ? score[best] / xn : 0.0;
+        if (best >= 0) cs = xn2 == 0.0 ? 0.0 : score[best] / xn;
         else cs = NAN;
         int keep = (best >= 0) && ((float)cs >= eps32);
         if (keep) {

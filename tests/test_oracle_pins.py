@@ -362,6 +362,10 @@ def test_nan_row_is_dropped():
     r = orc.compress(X, np.array([0, 9]), 0.0)
     assert r["f"][5] == -1 and r["alpha"][5] == 0.0
     assert np.all(r["f"][np.arange(20) != 5] >= 0)
+    # even when a zero generator offers a finite score of 0
+    X[11] = 0.0
+    r = orc.compress(X, np.array([0, 9, 11]), 0.0)
+    assert r["f"][5] == -1 and r["alpha"][5] == 0.0
 
 
 def test_no_generators_drops_everything():
