@@ -1,0 +1,210 @@
+"""PAMM (Point-Approximate Matrix Multiplication) for AMD Instinct MI355X.
+
+Thin Python binding over the C ABI of ``libpamm.so`` (see ``include/pamm.h``).
+It only marshals arguments: PyTorch supplies device memory and the current
+HIP stream, and every step of the computation runs in the library's HIP
+kernels.  There is no CPU fallback; if the library is missing the calls
+raise.
+
+Method: "QKV Projections Require a Fraction of Their Memory", section 2
+"Metodologia", sub-part "Algoritmo in Due Fasi" -- compress the saved inputs
+X of a QKV projection into generator rows C plus an (index, scale) pair per
+token, then approximate the weight gradient C^T B~ from that compressed form.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "PammError", "F32", "BF16", "MAX_K", "load_library", "library_path", "abi_version",
+    "sample_generators", "compress", "wgrad", "decompress",
+    "compress_workspace_size", "wgrad_workspace_size", "compressed_nbytes",
+]
+
+F32 = 0
+BF16 = 1
+MAX_K = 4096
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpamm.so")
+_lib = None
+
+_EXPORTS = {
+    # name: (restype, argtypes)
+    "pamm_abi_version": (ctypes.c_int, []),
+    "pamm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pamm_sample_generators": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p]),
+    "pamm_compress_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    "pamm_compress": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]),
+    "pamm_wgrad_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                    ctypes.c_int]),
+    "pamm_wgrad": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]),
+    "pamm_decompress": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p]),
+}
+
+
+class PammError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = load_library().pamm_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpamm.so (built by ``activation_compression_pamm_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"PAMM HIP library not built: {_LIB_PATH} is missing "
+                               "(run `python -m activation_compression_pamm_amd.build`)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return load_library().pamm_abi_version()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PammError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"PAMM supports float32 and bfloat16 tensors, got {t.dtype}")
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _rows(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def sample_generators(n: int, k: int, seed: int):
+    """k distinct row ids of [0, n), ascending, drawn on the host (int32 CPU tensor)."""
+    torch = _torch()
+    out = torch.empty(max(k, 0), dtype=torch.int32)
+    _check(load_library().pamm_sample_generators(n, k, seed & (2**64 - 1), _ptr(out)), "pamm_sample_generators")
+    return out
+
+
+def compress_workspace_size(n: int, d: int, k: int, dtype: int) -> int:
+    return int(load_library().pamm_compress_workspace_size(n, d, k, dtype))
+
+
+def wgrad_workspace_size(n: int, k: int, d: int, d_out: int, dtype: int) -> int:
+    return int(load_library().pamm_wgrad_workspace_size(n, k, d, d_out, dtype))
+
+
+def compressed_nbytes(n: int, k: int, d: int, dtype: int) -> int:
+    """Bytes of the saved triple (C, f, alpha)."""
+    return k * d * (2 if dtype == BF16 else 4) + 8 * n
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return workspace
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def compress(X, gen_idx, eps: float, *, C=None, f=None, alpha=None, workspace=None, stream=None):
+    """Compress activations X [n x d] (CUDA/HIP tensor, bf16 or fp32).
+
+    gen_idx: int32 device tensor of k generator row ids (see sample_generators).
+    Returns (C [k x d], f [n] int32, alpha [n] fp32)."""
+    torch = _torch()
+    n, d, ldx = _rows(X, "X")
+    dt = _dtype_code(X)
+    gen_idx = gen_idx.to(device=X.device, dtype=torch.int32).contiguous()
+    k = gen_idx.numel()
+    if C is None:
+        C = torch.empty((k, d), dtype=X.dtype, device=X.device)
+    if f is None:
+        f = torch.empty(n, dtype=torch.int32, device=X.device)
+    if alpha is None:
+        alpha = torch.empty(n, dtype=torch.float32, device=X.device)
+    ws = _workspace(compress_workspace_size(n, d, k, dt), X.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load_library().pamm_compress(_ptr(X), n, d, ldx, dt, _ptr(gen_idx), k, float(eps), _ptr(C), _ptr(f),
+                                      _ptr(alpha), _ptr(ws), nbytes, _stream_ptr(stream))
+    _check(st, "pamm_compress")
+    return C, f, alpha
+
+
+def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, workspace=None, stream=None):
+    """Approximate weight gradient dW = C^T B~ [d x d_out] (fp32) from the
+    compressed triple and the output gradient dY [n x d_out]."""
+    torch = _torch()
+    k, d = C.shape
+    n, d_out, lddy = _rows(dY, "dY")
+    dt = _dtype_code(dY)
+    if C.dtype != dY.dtype:
+        raise TypeError("C and dY must share a dtype")
+    if dW is None:
+        dW = torch.empty((d, d_out), dtype=torch.float32, device=dY.device)
+    _, _, lddw = _rows(dW, "dW")
+    ws = _workspace(wgrad_workspace_size(n, k, d, d_out, dt), dY.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load_library().pamm_wgrad(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, _ptr(dY), d_out, lddy, dt, _ptr(dW), lddw,
+                                   1 if accumulate else 0, _ptr(ws), nbytes, _stream_ptr(stream))
+    _check(st, "pamm_wgrad")
+    return dW
+
+
+def decompress(C, f, alpha, *, out=None, stream=None):
+    """Reconstruction X~_i = alpha_i C_f(i) (zero rows where f = -1)."""
+    torch = _torch()
+    k, d = C.shape
+    n = f.numel()
+    dt = _dtype_code(C)
+    if out is None:
+        out = torch.empty((n, d), dtype=C.dtype, device=f.device)
+    _, _, ldxt = _rows(out, "out")
+    st = load_library().pamm_decompress(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, dt, _ptr(out), ldxt,
+                                        _stream_ptr(stream))
+    _check(st, "pamm_decompress")
+    return out

@@ -1,0 +1,90 @@
+// pamm_kernels.hpp -- argument blocks and launchers of the PAMM kernels.
+// Host code validates everything before calling a launcher; launchers only
+// enqueue work on the given stream and report hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pamm {
+
+// Generators handled by one compress workgroup; larger k is split into tiles
+// whose winners are merged.
+constexpr int kMaxTileGens = 256;
+// Rows of one chunk of a generator's row list in the wgrad scatter-reduce.
+constexpr int kChunkRows = 256;
+// Rows handled by one block of the wgrad counting sort.
+constexpr int kSortBlockRows = 1024;
+// Generator-product K step (chunks per MFMA step).
+constexpr int kGemmKStep = 16;
+
+struct PartialBest {
+    float score;  // best |<x,c>|/|c| in the tile, -1 if none
+    int32_t gen;  // its generator slot, -1 if none
+    float alpha;  // <x,c>/|c|^2 for it
+};
+
+struct CompressArgs {
+    const void* X;
+    int64_t n, d;
+    int64_t ldx_bytes;  // leading dimension of X in bytes
+    int64_t row_bytes;  // d * element size
+    const int32_t* gen_idx;
+    int k;
+    float eps;
+    void* C;       // [k x d] output (may be null: not written)
+    int c_vec_ok;  // C rows are 16-byte aligned
+    int32_t* f;
+    float* alpha;
+    PartialBest* partial;  // [ntiles x n] when k > kMaxTileGens
+    float* xn2;            // [n] when k > kMaxTileGens
+};
+
+hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st);
+
+// Workspace carve-up of pamm_wgrad (all offsets 256-byte aligned).
+struct WgradLayout {
+    int64_t nb;         // sort blocks
+    int64_t max_chunks; // upper bound on row chunks
+    size_t off_hist, off_seg, off_nchunks, off_chunk_gen, off_chunk_begin, off_chunk_count;
+    size_t off_perm, off_palpha, off_P;
+    int64_t ldp;        // row stride of the chunk partial sums P (floats)
+    size_t total;
+};
+
+WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d_out);
+
+struct WgradArgs {
+    const void* C;
+    const int32_t* f;
+    const float* alpha;
+    int64_t n;
+    int k;
+    int64_t d;
+    const void* dY;
+    int64_t d_out;
+    int64_t lddy_bytes;
+    float* dW;
+    int64_t lddw;
+    int accumulate;
+    char* ws;
+    WgradLayout L;
+    int num_cus;
+};
+
+hipError_t run_wgrad(const WgradArgs& a, int dtype, hipStream_t st);
+
+struct DecompressArgs {
+    const void* C;
+    const int32_t* f;
+    const float* alpha;
+    int64_t n;
+    int k;
+    int64_t d;
+    void* Xt;
+    int64_t ldxt_bytes;
+};
+
+hipError_t run_decompress(const DecompressArgs& a, int dtype, hipStream_t st);
+
+}  // namespace pamm

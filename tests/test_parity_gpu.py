@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Each case prints its name, shapes and seeds before touching the GPU.  Small
+and medium cases compare every output; the full-size workloads compare
+sampled rows of (f, alpha) and sampled columns of dW, computed by the oracle
+one by one, plus properties that hold at any size.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import activation_compression_pamm_amd as pamm
+from activation_compression_pamm_amd import synth
+from oracle import oracle as orc
+
+from gpu_util import check_compress, check_wgrad, rel, run_gpu, to_dev, to_host, TOL
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def full_case(X, dY, gen_idx, eps, label):
+    n, d = X.shape
+    say(label, f"n={n} d={d} d_out={dY.shape[1]} k={gen_idx.size} eps={eps} dtype={X.dtype}")
+    out = run_gpu(X, dY, gen_idx, eps)
+    C_g, f_g, a_g = to_host(out["C"]), to_host(out["f"]), to_host(out["alpha"])
+    stats = check_compress(X, gen_idx, eps, C_g, f_g, a_g)
+    e_iso = check_wgrad(C_g, f_g, a_g, dY, to_host(out["dW"]))
+    # end to end: oracle compress + oracle wgrad, independent of the GPU
+    r = orc.compress(X, gen_idx, eps)
+    dW_o = orc.wgrad(r["C"], r["f"], r["alpha"], dY)
+    e_e2e = rel(to_host(out["dW"]), dW_o)
+    dt = "bf16" if X.dtype == np.uint16 else "f32"
+    if stats["inband_mismatches"] == 0:
+        # with identical indices the end-to-end result must meet the tolerance;
+        # an in-band flip legitimately moves a whole row to another generator
+        assert e_e2e <= TOL[dt], f"end-to-end dW error {e_e2e}"
+    # reconstruction: bit-exact against the oracle fed the GPU's triple
+    xt = to_host(pamm.decompress(out["C"], out["f"], out["alpha"]))
+    _, xt_o = orc.decompress(C_g, f_g, a_g)
+    assert np.array_equal(xt, xt_o)
+    say(label, "ok", stats, f"dW iso {e_iso:.2e} e2e {e_e2e:.2e}")
+    return out, stats
+
+
+# --------------------------------------------------------------------------
+# the small workloads, every output compared
+# --------------------------------------------------------------------------
+
+def test_tiny_fp32_config():
+    X, dY, p = synth.make_config("tiny_fp32")
+    g = pamm.sample_generators(p["n"], p["k"], synth.generator_seed("tiny_fp32")).numpy()
+    full_case(X, dY, g, p["eps"], "tiny_fp32")
+
+
+def test_gpt2_small_qkv_config():
+    X, dY, p = synth.make_config("gpt2_small_qkv")
+    g = pamm.sample_generators(p["n"], p["k"], synth.generator_seed("gpt2_small_qkv")).numpy()
+    full_case(X, dY, g, p["eps"], "gpt2_small_qkv")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,d,dout,k,eps", [
+    (1000, 200, 296, 24, 0.1),     # ragged rows, columns, outputs and generator tile
+    (777, 72, 136, 5, 0.0),
+    (2500, 384, 520, 64, 0.3),
+    (1536, 256, 256, 128, 0.1),
+    (1100, 136, 264, 256, 0.05),   # one full 256-generator tile
+    (2048, 256, 384, 300, 0.1),    # two generator tiles + merge
+    (3000, 128, 200, 1024, 0.1),   # four tiles, many small segments
+])
+def test_ragged_shapes(dtype, n, d, dout, k, eps):
+    X = synth.clustered_activations(n, d, max(4, k // 2), seed=n + d, dtype=dtype)
+    dY = synth.gradients(n, dout, seed=n + dout, dtype=dtype)
+    g = pamm.sample_generators(n, k, seed=k + 7).numpy()
+    full_case(X, dY, g, eps, f"ragged-{dtype}")
+
+
+def test_long_segments_split_into_chunks():
+    # one generator collects thousands of rows: its row list is cut into
+    # several chunks whose partial sums the generator product adds up
+    n, d, dout = 6000, 128, 192
+    X = synth.clustered_activations(n, d, 2, seed=3, dtype="bf16")
+    dY = synth.gradients(n, dout, seed=4, dtype="bf16")
+    g = np.array([0, 1, 2], dtype=np.int32)
+    full_case(X, dY, g, 0.0, "long-segments")
+
+
+# --------------------------------------------------------------------------
+# degenerate cases the method has
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_k_equals_n_gives_exact_product(dtype):
+    n, d, dout = 512, 64, 96
+    X = synth.random_matrix(n, d, 11, dtype)
+    dY = synth.random_matrix(n, dout, 12, dtype)
+    g = np.arange(n, dtype=np.int32)
+    say("k=n", dtype)
+    out = run_gpu(X, dY, g, 0.0)
+    f_g, a_g = to_host(out["f"]), to_host(out["alpha"])
+    assert np.array_equal(f_g, np.arange(n))
+    assert np.all(a_g == 1.0)   # |c|^2 uses the same MFMA arithmetic as the dot products
+    exact = orc.to_f64(X).T @ orc.to_f64(dY)
+    e = rel(to_host(out["dW"]), exact)
+    assert e <= (1e-4 if dtype == "bf16" else 1e-5), e
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scaled_copies_and_self_rows_exact(dtype):
+    n, d = 700, 96
+    X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 21, "bf16")) if dtype == "bf16" else \
+        synth.random_matrix(n, d, 21, "f32").copy()
+    g = np.array([3, 50, 99, 400, 650], dtype=np.int32)
+    plan = {10: (0, 2.0), 11: (1, -4.0), 12: (2, 0.5), 13: (3, -0.25), 600: (4, 8.0), 699: (0, -1.0)}
+    for row, (j, s) in plan.items():
+        X32[row] = np.float32(s) * X32[g[j]]
+    X = synth.f32_to_bf16_bits(X32) if dtype == "bf16" else X32
+    say("scaled-copies", dtype)
+    out = run_gpu(X, None, g, 0.0)
+    f_g, a_g = to_host(out["f"]), to_host(out["alpha"])
+    for row, (j, s) in plan.items():
+        assert f_g[row] == j and a_g[row] == s, (row, f_g[row], a_g[row])
+    assert np.array_equal(f_g[g], np.arange(5)) and np.all(a_g[g] == 1.0)
+    xt = to_host(pamm.decompress(out["C"], out["f"], out["alpha"]))
+    for row in list(plan) + list(g):
+        assert np.array_equal(xt[row], X[row])
+
+
+def test_duplicate_generators_and_zero_and_nan_rows():
+    n, d, dout = 300, 64, 80
+    X = synth.random_matrix(n, d, 31, "f32").copy()
+    X[40] = X[7]            # duplicate rows, both generators
+    X[41] = 4 * X[7]        # collinear with both
+    X[100] = 0.0            # zero generator
+    X[101] = 0.0            # zero row
+    X[102, 5] = np.nan      # NaN row
+    g = np.array([7, 40, 100, 200], dtype=np.int32)
+    dY = synth.random_matrix(n, dout, 32, "f32")
+    for eps in (0.0, 0.2):
+        say("degenerate", eps)
+        out = run_gpu(X, dY, g, eps)
+        f_g, a_g = to_host(out["f"]), to_host(out["alpha"])
+        assert f_g[7] == 0 and f_g[40] == 0 and f_g[41] == 0 and a_g[41] == 4.0
+        assert f_g[102] == -1 and a_g[102] == 0.0
+        if eps == 0.0:
+            assert f_g[101] == 0 and a_g[101] == 0.0
+        else:
+            assert f_g[101] == -1 and f_g[100] == -1
+        assert not np.any(f_g == 2)   # the zero generator never wins a nonzero row
+        check_compress(X, g, eps, to_host(out["C"]), f_g, a_g)
+        check_wgrad(to_host(out["C"]), f_g, a_g, dY, to_host(out["dW"]))
+
+
+def test_no_generators_and_single_row():
+    X = synth.random_matrix(50, 16, 41, "bf16")
+    dY = synth.random_matrix(50, 24, 42, "bf16")
+    say("k=0")
+    out = run_gpu(X, dY, np.zeros(0, dtype=np.int32), 0.0)
+    assert np.all(to_host(out["f"]) == -1) and np.all(to_host(out["alpha"]) == 0)
+    assert np.all(to_host(out["dW"]) == 0)
+    say("n=1")
+    X1, dY1 = X[:1], dY[:1]
+    out = run_gpu(X1, dY1, np.array([0], dtype=np.int32), 0.5)
+    assert to_host(out["f"])[0] == 0 and to_host(out["alpha"])[0] == 1.0
+    e = rel(to_host(out["dW"]), orc.to_f64(X1).T @ orc.to_f64(dY1))
+    assert e < 1e-4
+
+
+def test_eps_above_one_drops_everything():
+    X, dY, p = synth.make_config("gpt2_small_qkv", rows=2048)
+    g = pamm.sample_generators(2048, 16, 5).numpy()
+    say("eps>1")
+    out = run_gpu(X, dY, g, 1.5)
+    assert np.all(to_host(out["f"]) == -1)
+    assert np.all(to_host(out["dW"]) == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,dout", [(128, 160), (123, 157), (5, 3)])
+def test_accumulate_and_strided_views(dtype, d, dout):
+    # strided views whose row lengths need not be multiples of 16 bytes: the
+    # leading dimensions are, as the C ABI requires
+    n, k = 900, 12
+    ldx = (d + 7) // 8 * 8 + 16      # multiples of 16 bytes for both dtypes
+    lddy = (dout + 7) // 8 * 8 + 16
+    Xbig = synth.clustered_activations(n, ldx, 8, seed=51 + d, dtype=dtype)
+    dYbig = synth.gradients(n, lddy, seed=52, dtype=dtype)
+    X = np.ascontiguousarray(Xbig[:, :d])
+    dY = np.ascontiguousarray(dYbig[:, :dout])
+    g = pamm.sample_generators(n, k, 53).numpy()
+    say("strided", dtype, f"d={d} ldx={ldx} d_out={dout} lddy={lddy}")
+    Xd = to_dev(Xbig)[:, :d]
+    dYd = to_dev(dYbig)[:, :dout]
+    gd = torch.from_numpy(g).cuda()
+    C, f, a = pamm.compress(Xd, gd, 0.1)
+    lddw = dout + 8 - dout % 4
+    dW0 = torch.full((d, lddw), 3.0, device="cuda")[:, :dout]
+    pamm.wgrad(C, f, a, dYd, dW=dW0, accumulate=True)
+    xt_big = torch.full((n, ldx), 7.0, device="cuda", dtype=Xd.dtype)
+    pamm.decompress(C, f, a, out=xt_big[:, :d])
+    torch.cuda.synchronize()
+    C_g, f_g, a_g = to_host(C), to_host(f), to_host(a)
+    check_compress(X, g, 0.1, C_g, f_g, a_g)
+    ref = orc.wgrad(C_g, f_g, a_g, dY) + 3.0
+    assert rel(to_host(dW0), ref) < 1e-4
+    xt = to_host(xt_big)
+    _, xt_o = orc.decompress(C_g, f_g, a_g)
+    assert np.array_equal(xt[:, :d], xt_o)
+    # nothing written past the row length
+    assert np.all(orc.to_f64(xt[:, d:]) == 7.0)
+
+
+def test_deterministic_bitwise():
+    X, dY, p = synth.make_config("gpt2_small_qkv")
+    g = pamm.sample_generators(p["n"], p["k"], 9).numpy()
+    say("determinism")
+    a = run_gpu(X, dY, g, p["eps"])
+    b = run_gpu(X, dY, g, p["eps"])
+    for key in ("C", "f", "alpha", "dW"):
+        assert torch.equal(a[key], b[key]), key
+
+
+# --------------------------------------------------------------------------
+# full-size workloads: sampled outputs + properties
+# --------------------------------------------------------------------------
+
+def sampled_case(name, k=None, nrows=1536, ncols=12):
+    X, dY, p = synth.make_config(name, k=k)
+    n, d, dout = p["n"], p["d"], p["d_out"]
+    k = p["k"]
+    g = pamm.sample_generators(n, k, synth.generator_seed(name)).numpy()
+    say(name, f"n={n} d={d} d_out={dout} k={k} eps={p['eps']} (sampled)")
+    out = run_gpu(X, dY, g, p["eps"])
+    C_g, f_g, a_g = to_host(out["C"]), to_host(out["f"]), to_host(out["alpha"])
+    rng = np.random.default_rng(n + k)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, nrows, replace=False)]))
+    stats = check_compress(X, g, p["eps"], C_g, f_g, a_g, rows=rows)
+    cols = np.unique(np.concatenate([[0, dout - 1], rng.choice(dout, ncols, replace=False)]))
+    e = check_wgrad(C_g, f_g, a_g, dY, to_host(out["dW"]), cols=cols)
+    # properties at full size: dropped rows have alpha 0, indices in range,
+    # and a rerun is bitwise identical
+    assert np.all((f_g >= -1) & (f_g < k))
+    assert np.all(a_g[f_g < 0] == 0)
+    again = run_gpu(X, dY, g, p["eps"])
+    for key in ("f", "alpha", "dW"):
+        assert torch.equal(out[key], again[key]), key
+    say(name, "ok", stats, f"dW(sampled cols) {e:.2e}")
+    return stats
+
+
+def test_llama7b_qkv_full_size():
+    sampled_case("llama7b_qkv")
+
+
+@pytest.mark.parametrize("k", [1024, 256, 128, 64])
+def test_llama1b_sweep_full_size(k):
+    sampled_case("llama1b_sweep", k=k)
+
+
+def test_longseq_gqa_full_size():
+    sampled_case("longseq_gqa", nrows=1024, ncols=8)
