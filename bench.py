@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of the PAMM hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+pamm_compress (similarity contraction + fused argmax/alpha/eps epilogue) and
+pamm_wgrad (counting sort of kept rows, alpha-weighted segmented reduction,
+generator product) on the llama-7B QKV workload (n = 16 x 2048 tokens,
+d = 4096, d_out = 3 x 4096, k = 64 generators (512x), eps = 0.1, bf16),
+with every input resident in HBM before timing starts.  Generator sets for
+all steps are drawn on the host beforehand and uploaded.
+
+Prints one JSON line: tokens/s for the whole job, per-call times, a roofline
+entry for the dominant kernel (HIP events around its launches on the stream
+it runs on) and the CPU oracle timed on a bounded sample of the same
+workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "PAMM compress+wgrad tokens/sec; MFMA % peak and HBM GB/s % peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+# factor turning the FETCH_SIZE/WRITE_SIZE counters into bytes, from a plain
+# copy of known size; filled from profiles/ when the counters were taken
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_llama7b_qkv_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama7b_qkv")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle's timed sample")
+    p.add_argument("--cpu-cols", type=int, default=6144, help="dW columns of the oracle's timed sample")
+    return p.parse_args()
+
+
+def algorithmic(p, kept):
+    """Bytes and flops each call must move/compute (2-byte elements)."""
+    n, d, dout, k = p["n"], p["d"], p["d_out"], p["k"]
+    s = 2 if p["dtype"] == "bf16" else 4
+    compress_bytes = n * d * s + k * d * s + 8 * n          # read X, write C, write f and alpha
+    compress_flops = 2.0 * n * d * k
+    nk = int(round(kept * n))
+    reduce_bytes = nk * dout * s + 8 * n                     # read kept dY rows, f and alpha
+    product_bytes = 4 * d * dout                             # write dW (fp32)
+    product_flops = 2.0 * d * k * dout
+    return compress_bytes, compress_flops, reduce_bytes, product_bytes, product_flops
+
+
+def cpu_baseline(X, dY, gen_idx, p, rows, cols):
+    """Time the oracle (single-threaded C, fp64) on a bounded sample and scale
+    it to the full step: compress on `rows` rows, the B~ sums of those rows on
+    `cols` output columns, and the generator product on `cols` columns."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    n, dout = p["n"], p["d_out"]
+    rng = np.random.default_rng(0)
+    R = np.sort(rng.choice(n, rows, replace=False))
+    Q = np.sort(rng.choice(dout, cols, replace=False))
+    t0 = time.perf_counter()
+    r = orc.compress(X, gen_idx, p["eps"], rows=R)
+    t1 = time.perf_counter()
+    C = r["C"]
+    orc.wgrad(C, r["f"], r["alpha"], np.ascontiguousarray(dY[R]), cols=Q)
+    t2 = time.perf_counter()
+    empty = np.zeros(0, dtype=np.int32)
+    orc.wgrad(C, empty, np.zeros(0, dtype=np.float32), np.zeros((0, dout), dtype=dY.dtype), cols=Q)
+    t3 = time.perf_counter()
+    t_comp, t_w, t_prod = t1 - t0, t2 - t1, t3 - t2
+    t_sum = max(t_w - t_prod, 0.0)
+    est = t_comp * (n / rows) + t_sum * (n / rows) * (dout / cols) + t_prod * (dout / cols)
+    return {
+        "value": n / est,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"compress of {rows} of {n} rows, B~ sums of those rows on {cols} of {dout} output columns, "
+                   f"generator product on {cols} columns; each part scaled to the full step "
+                   f"(measured {t_comp + t_w + t_prod:.1f} s, estimated full step {est:.1f} s)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import activation_compression_pamm_amd as pamm
+    from activation_compression_pamm_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    name = args.workload
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    X, dY, p = synth.make_config(name)
+    n, d, dout, k, eps = p["n"], p["d"], p["d_out"], p["k"], p["eps"]
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    Xd, dYd = dev(X), dev(dY)
+    nsets = args.warmup + args.steps
+    t_s0 = time.perf_counter()
+    gens_host = [pamm.sample_generators(n, k, synth.generator_seed(name) + i) for i in range(nsets)]
+    t_sample = (time.perf_counter() - t_s0) / nsets
+    gens = torch.stack(gens_host).cuda()
+    dt_code = pamm.BF16 if p["dtype"] == "bf16" else pamm.F32
+    C = torch.empty((k, d), dtype=Xd.dtype, device="cuda")
+    f = torch.empty(n, dtype=torch.int32, device="cuda")
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    dW = torch.empty((d, dout), dtype=torch.float32, device="cuda")
+    cws = torch.empty(max(pamm.compress_workspace_size(n, d, k, dt_code), 1), dtype=torch.uint8, device="cuda")
+    wws = torch.empty(pamm.wgrad_workspace_size(n, k, d, dout, dt_code), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pamm.compress(Xd, gens[i], eps, C=C, f=f, alpha=a, workspace=cws)
+        if ev is not None:
+            ev[1].record(stream)
+        pamm.wgrad(C, f, a, dYd, dW=dW, workspace=wws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kept = float((f >= 0).float().mean().item())
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+    t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps  # ms
+    t_wgrad = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    kept = float((f >= 0).float().mean().item())
+
+    cb, cf, rb, pb, pf = algorithmic(p, kept)
+    comp_gbs = cb / (t_comp * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "compress_kernel (pamm_compress)", "achieved": round(comp_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": cb, "avg_launch_us": round(t_comp * 1e3, 2)}
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_source_hash") == source_hash():
+                roofline["traffic"] = tr["bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            pass
+
+    out = {
+        "metric": METRIC,
+        "value": round(n / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p["dtype"],
+        "data": "synthetic (clustered activations, Gaussian gradients; seeded)",
+        "config": {"workload": name, "n_tokens": n, "d": d, "d_out": dout, "k": k, "eps": eps,
+                   "compression": f"{n // k}x"},
+        "roofline": roofline,
+        "calls": {
+            "compress_us": round(t_comp * 1e3, 2),
+            "compress_gbs": round(comp_gbs, 1),
+            "compress_mfma_frac": round(cf / (t_comp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "wgrad_us": round(t_wgrad * 1e3, 2),
+            "wgrad_alg_gbs": round((rb + pb) / (t_wgrad * 1e-3) / 1e9, 1),
+            "kept_fraction": round(kept, 4),
+            "host_sampling_us": round(t_sample * 1e6, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(X, dY, gens_host[0].numpy(), p, args.cpu_rows, args.cpu_cols)
+    print(json.dumps(out), flush=True)
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "activation_compression_pamm_amd", "csrc")
+    for fn in sorted(os.listdir(src)):
+        if fn.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(src, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()
