@@ -8,9 +8,16 @@
 //
 // One kernel does the whole step.  A workgroup owns BM rows of X and a tile
 // of up to KN generators:
-//   * X and C (= rows gen_idx of X) stream through an NS-deep LDS ring with
-//     direct global->LDS 16-byte loads (no VGPR round trip), 128 bytes of each
-//     row per stage, XOR-swizzled so MFMA fragment reads avoid bank clashes.
+//   * X and C (= rows gen_idx of X) are fetched from HBM into VGPRs as full
+//     128-byte lines (8 lanes per row, the pattern HBM serves fastest; rows
+//     fetched in MFMA-fragment order, 64 bytes per row per instruction, ran
+//     at about 70% of that rate), PD stages ahead in a register ring, then
+//     written to a double-buffered LDS tile, XOR-swizzled so MFMA fragment
+//     reads avoid bank clashes.  Every load lands in registers, so the
+//     compiler tracks every wait; each trip issues the same loads.
+//   * Workgroups walk the d stages in a rotated order: rows are a leading
+//     dimension apart, and in lock-step all workgroups would read the same
+//     column range and crowd the same memory channels.
 //   * S = X C^T accumulates in MFMA registers (bf16 16x16x32, or fp32
 //     16x16x4); it is never written to memory.
 //   * |c_j|^2 comes from extra MFMAs of the C fragments with themselves, the
@@ -21,35 +28,26 @@
 //     (lowest index on ties, NaN never wins), cosine test against eps, alpha =
 //     S_if / |c_f|^2.
 // When k exceeds one generator tile the per-tile winners go to a small
-// workspace and pamm_compress_merge picks the overall winner.
+// workspace and compress_merge_kernel picks the overall winner.
 #include <type_traits>
 
 #include "pamm_device.hpp"
 #include "pamm_kernels.hpp"
 
+#ifndef PAMM_COMPRESS_ROTATE
+#define PAMM_COMPRESS_ROTATE 1
+#endif
+
 namespace pamm {
 
 namespace {
 
-constexpr int kRowBytes = 128;  // bytes of every row staged per pipeline stage
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
-// expcnt and lgkmcnt left at their maxima).
-template <int N>
-struct VmWait {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    static constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-};
-
-template <int N>
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(VmWait<N>::imm); }
-
-// Workgroup barrier for the DMA ring.  Each wave has already waited for its
-// own DMA of the stage (wait_vm) and, where it wrote LDS itself, for those
-// stores (lgkmcnt 0), so the barrier needs no memory fence; a full
-// __syncthreads() fence would also drain the DMA of later stages.  The empty
-// asm statements keep the compiler from moving memory accesses across it.
+// Workgroup barrier for the staged tiles.  Each wave has already waited for
+// its own LDS stores (wait_lds), so the barrier needs no memory fence; the
+// fence of __syncthreads() would also wait for every outstanding global
+// load, i.e. drain the register prefetch.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
 __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -57,12 +55,6 @@ __device__ __forceinline__ void ring_barrier() {
 }
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14)); }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
 
 template <int DT>
 __device__ __forceinline__ void mma16(const uint4& a, const uint4& b, f32x4& acc) {
@@ -88,8 +80,13 @@ __device__ __forceinline__ float sumsq16(const uint4& v) {
     return s;
 }
 
-// Byte offset in a staged tile of 16-byte chunk `q` (0..7) of tile row `r`.
-__device__ __forceinline__ int swz(int r, int q) { return r * kRowBytes + ((q ^ (r & 7)) << 4); }
+// Byte offset in a staged tile (RB bytes per row) of 16-byte chunk `q` of
+// tile row `r`: chunks are XOR-swizzled by the row so that the 16 rows of an
+// MFMA fragment read fall into different LDS banks.
+template <int RB>
+__device__ __forceinline__ int swz(int r, int q) {
+    return r * RB + ((q ^ (r & (RB / 16 - 1))) << 4);
+}
 
 // Call f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, typename F>
@@ -102,36 +99,92 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 }  // namespace
 
-template <int DT, int WM, int NW, int KN, int NS>
-__global__ __launch_bounds__(64 * NW) void compress_kernel(CompressArgs a) {
+// Per-row winner among a generator tile, then the eps test and alpha.
+// acc[mt][nt][i] holds S for row 16*mt + 4*(lane/16) + i of the wave and
+// generator 16*nt + lane%16 of the tile; xn2r[mt] holds |x|^2 of row
+// 16*mt + lane%16.  The 16 lanes of a row reduce (score desc, index asc);
+// a NaN score never wins.
+template <int MT, int NTL>
+__device__ __forceinline__ void epilogue_rows(const CompressArgs& a, const f32x4 (&acc)[MT][NTL],
+                                              const float (&xn2r)[MT], const float* s_cn2, const float* s_rinv,
+                                              int64_t row_base, int gen0, int ktile, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rloc = mt * 16 + 4 * (lane >> 4) + i;
+            float bs = -1.0f, bd = 0.f;
+            int bg = 0x7fffffff;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                const int jl = nt * 16 + (lane & 15);
+                if (jl < ktile) {
+                    const float dot = acc[mt][nt][i];
+                    const float cn = s_cn2[jl];
+                    const float sc = cn > 0.f ? fabsf(dot) * s_rinv[jl] : 0.f;
+                    if (sc > bs) { bs = sc; bg = gen0 + jl; bd = dot; }
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                const float os = shfl_xor(bs, m);
+                const int og = shfl_xor(bg, m);
+                const float od = shfl_xor(bd, m);
+                if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = od; }
+            }
+            const float xn2 = __shfl(xn2r[mt], 4 * (lane >> 4) + i, 64);
+            const int64_t row = row_base + rloc;
+            if ((lane & 15) == i && row < a.n) {
+                const bool found = bg != 0x7fffffff;
+                float al = 0.f;
+                if (found) {
+                    const float cn = s_cn2[bg - gen0];
+                    al = cn > 0.f ? bd / cn : 0.f;
+                }
+                if (a.partial) {
+                    PartialBest pb;
+                    pb.score = found ? bs : -1.0f;
+                    pb.gen = found ? bg : -1;
+                    pb.alpha = al;
+                    a.partial[(int64_t)blockIdx.y * a.n + row] = pb;
+                    if (blockIdx.y == 0) a.xn2[row] = xn2;
+                } else {
+                    // cosine of the winner; 0 for a zero row, NaN (never kept) for a NaN row
+                    const float cs = xn2 == 0.f ? 0.f : bs / sqrtf(xn2);
+                    const bool keep = found && cs >= a.eps;
+                    a.f[row] = keep ? bg : -1;
+                    a.alpha[row] = keep ? al : 0.f;
+                }
+            }
+        }
+    }
+}
+
+// The compress kernel (see the file comment).  WM rows per wave, NW waves,
+// KN generators per tile, PD stages of register prefetch.
+template <int DT, int WM, int NW, int KN, int PD>
+__global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
+    constexpr int RB = 128;                           // bytes of each row per stage
+    constexpr int SUBS = RB / 64;
+    constexpr int CH = RB / 16;                       // 8 chunks per row
+    constexpr int RPI = 64 / CH;                      // rows per wave-wide load
     constexpr int BM = WM * NW;
     constexpr int MT = WM / 16;
     constexpr int NTL = KN / 16;
     constexpr int NDG = (NTL + NW - 1) / NW;
-    constexpr int XLD = BM / (8 * NW);               // X dma per wave per stage
-    constexpr int CLD = (KN + 8 * NW - 1) / (8 * NW);  // C dma per wave per stage (rounded up)
-    constexpr int LPS = XLD + CLD;
-    constexpr int E = kRowBytes / Elem<DT>::size;     // elements of a row per stage
+    constexpr int XPT = BM / (RPI * NW);              // X chunks per lane per stage
+    constexpr int CPT = (KN + RPI * NW - 1) / (RPI * NW);
+    constexpr int CROWS = CPT * NW * RPI;
+    constexpr int E = RB / Elem<DT>::size;
     constexpr int P = Elem<DT>::per16;
-    static_assert(BM % (8 * NW) == 0, "tile shape");
-    static_assert((NS - 2) * LPS < 64, "vmcnt window");
+    static_assert(BM % (RPI * NW) == 0 && PD % 2 == 0 && PD >= 2, "tile shape");
 
-    // One LDS object per ring slot: with the slot known at compile time the
-    // compiler can tell a DMA into one slot from reads of another, and does
-    // not drain the whole DMA queue before every LDS read.
-    constexpr int CROWS = CLD * NW * 8;
-    __shared__ __align__(16) char s_x0[BM * kRowBytes];
-    __shared__ __align__(16) char s_x1[BM * kRowBytes];
-    __shared__ __align__(16) char s_x2[BM * kRowBytes];
-    __shared__ __align__(16) char s_x3[NS > 3 ? BM * kRowBytes : 16];
-    __shared__ __align__(16) char s_c0[CROWS * kRowBytes];
-    __shared__ __align__(16) char s_c1[CROWS * kRowBytes];
-    __shared__ __align__(16) char s_c2[CROWS * kRowBytes];
-    __shared__ __align__(16) char s_c3[NS > 3 ? CROWS * kRowBytes : 16];
-    static_assert(NS == 3 || NS == 4, "ring depth");
+    __shared__ __align__(16) char s_x0[BM * RB];
+    __shared__ __align__(16) char s_x1[BM * RB];
+    __shared__ __align__(16) char s_c0[CROWS * RB];
+    __shared__ __align__(16) char s_c1[CROWS * RB];
     __shared__ float s_cn2[KN];
     __shared__ float s_rinv[KN];
-    __shared__ float s_xn2[BM];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -140,6 +193,7 @@ __global__ __launch_bounds__(64 * NW) void compress_kernel(CompressArgs a) {
     const int gen0 = blockIdx.y * KN;
     const int ktile = min(KN, a.k - gen0);
     const int nst = (int)((a.d + E - 1) / E);
+    const int last = nst - 1;
     const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
 
     // ---- copy out the generator rows C = X[gen_idx] (spread over all workgroups)
@@ -168,62 +222,57 @@ __global__ __launch_bounds__(64 * NW) void compress_kernel(CompressArgs a) {
         }
     }
 
-    // ---- per-lane source rows for the DMA (fixed for the whole d loop)
-    // DMA instruction `i` of this wave covers tile rows 8*(wave + NW*i) .. +8;
-    // lane L of it lands in row 8*(...) + L/8, swizzled slot L%8, and fetches
-    // chunk (L%8) ^ (row & 7) of that row.
-    const char* xsrc[XLD];
-    int xq[XLD];
+    // ---- rows this lane fetches: load i covers tile rows RPI*(wave + NW*i) + lane/8,
+    // 16-byte chunk lane%8 of each 128-byte stage
+    const int q8 = lane & 7;
+    const char* xsrc[XPT];
+    int xdst[XPT];
 #pragma unroll
-    for (int i = 0; i < XLD; ++i) {
-        const int r = 8 * (wave + NW * i) + (lane >> 3);
+    for (int i = 0; i < XPT; ++i) {
+        const int r = RPI * (wave + NW * i) + (lane >> 3);
         int64_t g = m0 + r;
         if (g >= a.n) g = a.n - 1;  // padding rows: any valid row, results unused
-        xsrc[i] = X + g * a.ldx_bytes;
-        xq[i] = (lane & 7) ^ (r & 7);
+        xsrc[i] = X + g * a.ldx_bytes + q8 * 16;
+        xdst[i] = swz<RB>(r, q8);
     }
-    const char* csrc[CLD];
-    int cq[CLD];
+    const char* csrc[CPT];
+    int cdst[CPT];
 #pragma unroll
-    for (int i = 0; i < CLD; ++i) {
-        const int r = 8 * (wave + NW * i) + (lane >> 3);
+    for (int i = 0; i < CPT; ++i) {
+        const int r = RPI * (wave + NW * i) + (lane >> 3);
         const int jj = min(r, max(ktile - 1, 0));  // padding generators: any valid one, masked later
         int64_t g = a.k > 0 ? a.gen_idx[gen0 + jj] : 0;
         g = g < 0 ? 0 : (g >= a.n ? a.n - 1 : g);
-        csrc[i] = X + g * a.ldx_bytes;
-        cq[i] = (lane & 7) ^ (r & 7);
+        csrc[i] = X + g * a.ldx_bytes + q8 * 16;
+        cdst[i] = swz<RB>(r, q8);
     }
+    // rotated stage order (workgroups start at different column ranges);
+    // padding stages past the end map to the last stage and are zeroed
+    const int rot = PAMM_COMPRESS_ROTATE ? (int)((blockIdx.x * 37u) % (unsigned)nst) : 0;
+    auto stage_of = [&](int s) { if (s >= nst) return last; int t = s + rot; return t >= nst ? t - nst : t; };
+    const int tail_elems = (int)(a.d - (int64_t)last * E);
 
-    auto xslot = [&](auto uc) -> char* {
-        constexpr int U = decltype(uc)::value;
-        if constexpr (U == 0) return s_x0;
-        else if constexpr (U == 1) return s_x1;
-        else if constexpr (U == 2) return s_x2;
-        else return s_x3;
-    };
-    auto cslot = [&](auto uc) -> char* {
-        constexpr int U = decltype(uc)::value;
-        if constexpr (U == 0) return s_c0;
-        else if constexpr (U == 1) return s_c1;
-        else if constexpr (U == 2) return s_c2;
-        else return s_c3;
-    };
+    uint4 xr[PD][XPT], cr[PD][CPT];
     auto issue = [&](int s, auto slotc) {
-        char* sx = xslot(slotc);
-        char* sc = cslot(slotc);
-        const int64_t colb = (int64_t)s * kRowBytes;
+        constexpr int U = decltype(slotc)::value;
+        int64_t off = (int64_t)stage_of(s) * RB + q8 * 16;
+        off = off >= a.row_bytes ? -(int64_t)q8 * 16 : (int64_t)stage_of(s) * RB;  // chunk past the row end: chunk 0
 #pragma unroll
-        for (int i = 0; i < XLD; ++i) {
-            int64_t off = colb + (xq[i] << 4);
-            if (off >= a.row_bytes) off = 0;  // past the row end: fetch chunk 0, zeroed below
-            dma16(xsrc[i] + off, sx + 8 * (wave + NW * i) * kRowBytes);
-        }
+        for (int i = 0; i < XPT; ++i) xr[U][i] = *reinterpret_cast<const uint4*>(xsrc[i] + off);
 #pragma unroll
-        for (int i = 0; i < CLD; ++i) {
-            int64_t off = colb + (cq[i] << 4);
-            if (off >= a.row_bytes) off = 0;
-            dma16(csrc[i] + off, sc + 8 * (wave + NW * i) * kRowBytes);
+        for (int i = 0; i < CPT; ++i) cr[U][i] = *reinterpret_cast<const uint4*>(csrc[i] + off);
+    };
+    // zero the elements of a chunk starting at stage element e0 that lie at or past `lim`
+    auto mask_chunk = [&](uint4& v, int e0, int lim) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            if (e0 + e >= lim) {
+                if constexpr (DT == DT_BF16) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                else w[e] = 0;
+            }
         }
+        v = make_uint4(w[0], w[1], w[2], w[3]);
     };
 
     f32x4 acc[MT][NTL];
@@ -238,79 +287,56 @@ __global__ __launch_bounds__(64 * NW) void compress_kernel(CompressArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xsq[mt] = 0.f;
 
-    // the C copy-out above used vector memory; drain it so the DMA counts are exact
-    wait_vm<0>();
+    static_for<0, PD>([&](auto uc) { issue(decltype(uc)::value, uc); });
 
-    // ---- prologue: stages 0 .. NS-2
-    static_for<0, NS - 1>([&](auto uc) {
-        if (decltype(uc)::value < nst) issue(decltype(uc)::value, uc);
-    });
-
-    const int tail_elems = (int)(a.d - (int64_t)(nst - 1) * E);  // valid elements in the last stage
-
-    for (int s0 = 0; s0 < nst; s0 += NS) {
-        static_for<0, NS>([&](auto uc) {
+    for (int s0 = 0; s0 < nst; s0 += PD) {
+        static_for<0, PD>([&](auto uc) {
             constexpr int U = decltype(uc)::value;
             const int s = s0 + U;
-            if (s < nst) {
-                char* sx = xslot(uc);
-                char* sc = cslot(uc);
-                // wait for this wave's DMA of stage s: stages s+1 .. min(s+NS-2, nst-1) may stay in flight
-                const int ahead = min(NS - 2, nst - 1 - s);
-                if constexpr (NS >= 4) {
-                    if (ahead >= 2) wait_vm<2 * LPS>();
-                    else if (ahead == 1) wait_vm<LPS>();
-                    else wait_vm<0>();
-                } else {
-                    if (ahead >= 1) wait_vm<LPS>();
-                    else wait_vm<0>();
+            char* sx = (U & 1) ? s_x1 : s_x0;
+            char* sc = (U & 1) ? s_c1 : s_c0;
+            const int lim = s >= nst ? 0 : (stage_of(s) < last ? E : tail_elems);
+            uint4 xw[XPT], cw[CPT];
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) xw[i] = xr[U][i];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) cw[i] = cr[U][i];
+            if (lim < E) {  // uniform: the last real stage and the padding stages
+#pragma unroll
+                for (int i = 0; i < XPT; ++i) mask_chunk(xw[i], q8 * P, lim);
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) mask_chunk(cw[i], q8 * P, lim);
+            }
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) *reinterpret_cast<uint4*>(sx + xdst[i]) = xw[i];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(sc + cdst[i]) = cw[i];
+            issue(s + PD, uc);  // register slot U is free again
+            wait_lds();
+            ring_barrier();
+#pragma unroll
+            for (int sub = 0; sub < SUBS; ++sub) {
+                const int q = sub * 4 + (lane >> 4);
+                uint4 xf[MT], cf[NTL], cd[NDG];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    xf[mt] = *reinterpret_cast<const uint4*>(sx + swz<RB>(wave * WM + mt * 16 + (lane & 15), q));
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+                    cf[nt] = *reinterpret_cast<const uint4*>(sc + swz<RB>(nt * 16 + (lane & 15), q));
+#pragma unroll
+                for (int g = 0; g < NDG; ++g) {
+                    const int nt = min(wave + g * NW, NTL - 1);
+                    cd[g] = *reinterpret_cast<const uint4*>(sc + swz<RB>(nt * 16 + (lane & 15), q));
                 }
-                ring_barrier();
-                if (s == nst - 1 && tail_elems < E) {
-                    // zero the elements past d in the last stage (both tiles)
-                    for (int r = tid; r < BM + CROWS; r += 64 * NW) {
-                        const int rr = r < BM ? r : r - BM;
-                        char* row = r < BM ? sx + r * kRowBytes : sc + rr * kRowBytes;
-                        for (int e = tail_elems; e < E; ++e) {
-                            const int byte = e * Elem<DT>::size;
-                            char* p = row + (((byte >> 4) ^ (rr & 7)) << 4) + (byte & 15);
-                            if constexpr (DT == DT_BF16) *reinterpret_cast<uint16_t*>(p) = 0;
-                            else *reinterpret_cast<uint32_t*>(p) = 0;
-                        }
-                    }
-                    wait_lds();
-                    ring_barrier();
-                }
-                if (s + NS - 1 < nst) issue(s + NS - 1, std::integral_constant<int, (U + NS - 1) % NS>{});
-
-                // ---- compute stage s from ring slot U
 #pragma unroll
-                for (int sub = 0; sub < kRowBytes / 64; ++sub) {
-                    const int q = sub * 4 + (lane >> 4);
-                    uint4 xf[MT];
+                for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const int r = wave * WM + mt * 16 + (lane & 15);
-                        xf[mt] = *reinterpret_cast<const uint4*>(sx + swz(r, q));
-                        xsq[mt] += sumsq16<DT>(xf[mt]);
-                    }
+                    for (int mt = 0; mt < MT; ++mt) mma16<DT>(xf[mt], cf[nt], acc[mt][nt]);
 #pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) {
-                        const int r = nt * 16 + (lane & 15);
-                        const uint4 cf = *reinterpret_cast<const uint4*>(sc + swz(r, q));
+                for (int g = 0; g < NDG; ++g) mma16<DT>(cd[g], cd[g], dacc[g]);
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) mma16<DT>(xf[mt], cf, acc[mt][nt]);
-                    }
-                    // |c|^2: wave w squares generator tiles w, w+NW, ...  MFMA
-                    // ignores the EXEC mask, so the tile is chosen through the
-                    // LDS address, never through a lane-dependent branch.
-#pragma unroll
-                    for (int g = 0; g < NDG; ++g) {
-                        const int nt = min(wave + g * NW, NTL - 1);
-                        const uint4 cd = *reinterpret_cast<const uint4*>(sc + swz(nt * 16 + (lane & 15), q));
-                        mma16<DT>(cd, cd, dacc[g]);
-                    }
-                }
+                for (int mt = 0; mt < MT; ++mt) xsq[mt] += sumsq16<DT>(xf[mt]);
             }
         });
     }
@@ -326,66 +352,16 @@ __global__ __launch_bounds__(64 * NW) void compress_kernel(CompressArgs a) {
             s_rinv[nt * 16 + c] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
         }
     }
+    float xn2r[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         float v = xsq[mt];
         v += shfl_xor(v, 16);
         v += shfl_xor(v, 32);
-        if (lane < 16) s_xn2[wave * WM + mt * 16 + lane] = v;
+        xn2r[mt] = v;
     }
     __syncthreads();
-
-    // ---- epilogue: per-row winner among this tile's generators
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rloc = wave * WM + mt * 16 + 4 * (lane >> 4) + i;
-            float bs = -1.0f, bd = 0.f;
-            int bg = 0x7fffffff;
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                const int jl = nt * 16 + (lane & 15);
-                if (jl < ktile) {
-                    const float dot = acc[mt][nt][i];
-                    const float cn = s_cn2[jl];
-                    const float sc = cn > 0.f ? fabsf(dot) * s_rinv[jl] : 0.f;
-                    if (sc > bs) { bs = sc; bg = gen0 + jl; bd = dot; }
-                }
-            }
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-                const float os = shfl_xor(bs, m);
-                const int og = shfl_xor(bg, m);
-                const float od = shfl_xor(bd, m);
-                if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = od; }
-            }
-            const int64_t row = m0 + rloc;
-            if ((lane & 15) == i && row < a.n) {
-                const bool found = bg != 0x7fffffff;
-                float al = 0.f;
-                if (found) {
-                    const float cn = s_cn2[bg - gen0];
-                    al = cn > 0.f ? bd / cn : 0.f;
-                }
-                const float xn2 = s_xn2[rloc];
-                if (a.partial) {
-                    PartialBest pb;
-                    pb.score = found ? bs : -1.0f;
-                    pb.gen = found ? bg : -1;
-                    pb.alpha = al;
-                    a.partial[(int64_t)blockIdx.y * a.n + row] = pb;
-                    if (blockIdx.y == 0) a.xn2[row] = xn2;
-                } else {
-                    // cosine of the winner; 0 for a zero row, NaN (never kept) for a NaN row
-                    const float cs = xn2 == 0.f ? 0.f : bs / sqrtf(xn2);
-                    const bool keep = found && cs >= a.eps;
-                    a.f[row] = keep ? bg : -1;
-                    a.alpha[row] = keep ? al : 0.f;
-                }
-            }
-        }
-    }
+    epilogue_rows<MT, NTL>(a, acc, xn2r, s_cn2, s_rinv, m0 + wave * WM, gen0, ktile, lane);
 }
 
 // Pick, per row, the best of the per-tile winners (tiles are in increasing
@@ -417,22 +393,40 @@ __global__ __launch_bounds__(256) void compress_empty_kernel(int64_t n, int32_t*
     if (row < n) { f[row] = -1; alpha[row] = 0.f; }
 }
 
-template <int DT, int WM, int NW, int KN, int NS>
-static hipError_t launch_compress(const CompressArgs& a, int ntiles, hipStream_t st) {
+template <int DT, int WM, int NW, int KN, int PD>
+static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStream_t st) {
     constexpr int BM = WM * NW;
     dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)ntiles);
-    hipLaunchKernelGGL((compress_kernel<DT, WM, NW, KN, NS>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((compress_rs_kernel<DT, WM, NW, KN, PD>), grid, dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
+
+// Tile shapes per generator-tile width: rows per wave, waves, generators,
+// register prefetch depth (stages).
+#ifndef PAMM_COMPRESS_RS16
+#define PAMM_COMPRESS_RS16 16, 8, 16, 4
+#endif
+#ifndef PAMM_COMPRESS_RS32
+#define PAMM_COMPRESS_RS32 16, 8, 32, 4
+#endif
+#ifndef PAMM_COMPRESS_RS64
+#define PAMM_COMPRESS_RS64 16, 8, 64, 4
+#endif
+#ifndef PAMM_COMPRESS_RS128
+#define PAMM_COMPRESS_RS128 16, 8, 128, 4
+#endif
+#ifndef PAMM_COMPRESS_RS256
+#define PAMM_COMPRESS_RS256 16, 8, 256, 4
+#endif
 
 template <int DT>
 static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, hipStream_t st) {
     switch (kn) {
-        case 16: return launch_compress<DT, 32, 4, 16, 4>(a, ntiles, st);
-        case 32: return launch_compress<DT, 32, 4, 32, 4>(a, ntiles, st);
-        case 64: return launch_compress<DT, 32, 4, 64, 4>(a, ntiles, st);
-        case 128: return launch_compress<DT, 32, 4, 128, 4>(a, ntiles, st);
-        default: return launch_compress<DT, 16, 8, 256, 3>(a, ntiles, st);
+        case 16: return launch_compress_rs<DT, PAMM_COMPRESS_RS16>(a, ntiles, st);
+        case 32: return launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
+        case 64: return launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
+        case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
+        default: return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);
     }
 }
 
