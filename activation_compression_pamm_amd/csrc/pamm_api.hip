@@ -134,10 +134,9 @@ int pamm_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int dtype, c
 }
 
 size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out, int dtype) {
-    (void)d;
     (void)dtype;
-    if (n < 0 || k < 0 || d_out < 1) return 0;
-    return pamm::wgrad_layout(n, k, d_out).total;
+    if (n < 0 || k < 0 || d < 1 || d_out < 1) return 0;
+    return pamm::wgrad_layout(n, k, d, d_out).total;
 }
 
 int pamm_wgrad(const void* C, const int32_t* f, const float* alpha, int64_t n, int64_t k, int64_t d, const void* dY,
@@ -152,7 +151,7 @@ int pamm_wgrad(const void* C, const int32_t* f, const float* alpha, int64_t n, i
     if (n > 0 && (!aligned(f, 4) || !aligned(alpha, 4) || !aligned(dY, 16) || lddy % per16(dtype) != 0))
         return PAMM_ERR_ALIGN;
     if (k > 0 && !aligned(C, 16)) return PAMM_ERR_ALIGN;
-    const pamm::WgradLayout L = pamm::wgrad_layout(n, k, d_out);
+    const pamm::WgradLayout L = pamm::wgrad_layout(n, k, d, d_out);
     if (!ws || ws_bytes < L.total) return PAMM_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return PAMM_ERR_ALIGN;
 

@@ -15,8 +15,6 @@ constexpr int kMaxTileGens = 256;
 constexpr int kChunkRows = 256;
 // Rows handled by one block of the wgrad counting sort.
 constexpr int kSortBlockRows = 1024;
-// Generator-product K step (chunks per MFMA step).
-constexpr int kGemmKStep = 16;
 
 struct PartialBest {
     float score;  // best |<x,c>|/|c| in the tile, -1 if none
@@ -47,12 +45,13 @@ struct WgradLayout {
     int64_t nb;         // sort blocks
     int64_t max_chunks; // upper bound on row chunks
     size_t off_hist, off_seg, off_nchunks, off_chunk_gen, off_chunk_begin, off_chunk_count;
-    size_t off_perm, off_palpha, off_P;
+    size_t off_perm, off_palpha, off_P, off_AT, off_BT;
     int64_t ldp;        // row stride of the chunk partial sums P (floats)
+    int64_t ks_cap;     // 16-chunk contraction steps the product operands hold
     size_t total;
 };
 
-WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d_out);
+WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out);
 
 struct WgradArgs {
     const void* C;

@@ -31,6 +31,14 @@
 #include "pamm_device.hpp"
 #include "pamm_kernels.hpp"
 
+// dW tile of one wave: 32*TM rows x 32*TN columns
+#ifndef PAMM_GEMM_TM
+#define PAMM_GEMM_TM 2
+#endif
+#ifndef PAMM_GEMM_TN
+#define PAMM_GEMM_TN 2
+#endif
+
 namespace pamm {
 
 namespace {
@@ -131,18 +139,25 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int64_t b = blockIdx.x;
 
-    // segment sizes and the rows of each generator that precede this block
-    for (int j = t; j < k; j += 256) {
-        int tot = 0, pre = 0;
-        for (int64_t bb = 0; bb < a.nb; ++bb) {
-            const int h = a.hist[bb * k + j];
-            tot += h;
-            if (bb < b) pre += h;
-        }
-        s_tot[j] = tot;
-        s_base[j] = pre;
-    }
+    // segment sizes and the rows of each generator that precede this block:
+    // the whole histogram is read with coalesced, independent loads and
+    // summed with LDS integer atomics (exact, so the order does not matter)
+    for (int j = t; j < k; j += 256) { s_tot[j] = 0; s_base[j] = 0; }
     for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
+    __syncthreads();
+    {
+        const int64_t total = a.nb * k;
+        const int64_t pre_end = b * k;  // entries of blocks before this one
+#pragma unroll 8
+        for (int64_t e = t; e < total; e += 256) {
+            const int h = a.hist[e];
+            if (h) {
+                const int j = (int)(e % k);
+                atomicAdd(&s_tot[j], h);
+                if (e < pre_end) atomicAdd(&s_base[j], h);
+            }
+        }
+    }
     __syncthreads();
 
     // block 0 cuts every generator's rows into chunks (before s_tot becomes starts)
@@ -153,8 +168,6 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
         const int total_chunks = block_exclusive_scan(s_nch, k, s_tmp);
         if (t == 0) *a.nchunks = total_chunks;
         __syncthreads();
-        // chunk rows are laid out after the segment starts, computed below;
-        // stash the offsets in s_tmp-free form: keep s_nch until starts are known
     }
 
     const int total_rows = block_exclusive_scan(s_tot, k, s_tmp);  // s_tot := segment starts
@@ -299,165 +312,225 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
 // ---------------------------------------------------------------------------
 // 4. generator product dW = sum_chunk c_gen(chunk) (x) P[chunk]
 // ---------------------------------------------------------------------------
-struct GemmArgs {
-    const void* C;  // [k x d]
+// 4a. Operands stored in MFMA-fragment order, so that every fragment a wave
+// needs is one contiguous 1 KB (64 lanes x 16 bytes) load.  For 32-row block
+// mb (rows of dW, i.e. d) or 32-column block nb (d_out) and contraction step
+// ks (16 chunks):
+//   bf16: lane l, piece 0:  A[32mb + l%32][16ks + 8(l/32) + 0..7]
+//   fp32: lane l, piece h:  A[32mb + l%32][16ks + 8h + 4(l/32) + 0..3]
+// with A[m][kk] = C[gen(kk)][m] and B[n][kk] = P[kk][n] (bf16: P split into
+// hi + lo bf16 terms, B holding all hi blocks, then all lo blocks); entries
+// past d, d_out or the chunk count are zero.
+struct PrepArgs {
+    const void* C;
     int64_t d;
     int64_t d_out;
     const int32_t* nchunks;
     const int32_t* chunk_gen;
     const float* P;
     int64_t ldp;
-    float* dW;
-    int64_t lddw;
-    int accumulate;
+    void* AF;       // A fragments
+    void* BF;       // B fragments
+    int64_t ks_cap; // contraction steps the buffers hold
 };
 
-namespace {
-constexpr int kGBM = 128;  // dW rows (d) per workgroup
-constexpr int kGBN = 128;  // dW columns (d_out) per workgroup
-constexpr int kGKP = 32;   // chunks per LDS panel
-}  // namespace
-
 template <int DT>
-__global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
-    // LDS panels stored transposed: [row of the tile][chunk], chunk contiguous.
-    constexpr int KPAD = DT == DT_BF16 ? kGKP + 8 : kGKP + 4;  // padded row length (elements)
-    typedef typename std::conditional<DT == DT_BF16, uint16_t, float>::type T;
-    __shared__ __align__(16) T sA[kGBM * KPAD];
-    __shared__ __align__(16) T sBh[kGBN * KPAD];
-    __shared__ __align__(16) T sBl[DT == DT_BF16 ? kGBN * KPAD : 8];
-
-    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-    const int64_t m0 = (int64_t)blockIdx.y * kGBM;
-    const int64_t n0 = (int64_t)blockIdx.x * kGBN;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+__global__ __launch_bounds__(256) void gemm_prep_kernel(PrepArgs a, int64_t a_items) {
+    constexpr int PIECES = DT == DT_BF16 ? 1 : 2;    // 16-byte pieces per lane per step
     const int nch = *a.nchunks;
+    const int ks_used = (nch + 15) >> 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // idx -> (block, step, piece, lane); lane fastest so stores are contiguous
+    const bool is_a = idx < a_items;
+    const int64_t j = is_a ? idx : idx - a_items;
+    const int lane = (int)(j & 63);
+    const int64_t rest = j >> 6;
+    const int piece = (int)(rest % PIECES);
+    const int64_t ks = (rest / PIECES) % a.ks_cap;
+    const int64_t blk = (rest / PIECES) / a.ks_cap;
+    if (ks >= ks_used) return;
+    const int64_t row = blk * 32 + (lane & 31);   // m (A) or n (B)
+    const int kk0 = (int)(ks * 16) + (DT == DT_BF16 ? 8 * (lane >> 5) : 8 * piece + 4 * (lane >> 5));
+    const int64_t slot = (blk * a.ks_cap + ks) * PIECES + piece;   // 1 KB slot index
+    if (is_a) {
+        if (blk * 32 >= a.d) return;
+        if constexpr (DT == DT_BF16) {
+            uint16_t v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = kk0 + e;
+                v[e] = (kk < nch && row < a.d)
+                           ? reinterpret_cast<const uint16_t*>(a.C)[(int64_t)a.chunk_gen[kk] * a.d + row] : (uint16_t)0;
+            }
+            reinterpret_cast<uint4*>(a.AF)[slot * 64 + lane] = *reinterpret_cast<uint4*>(v);
+        } else {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kk = kk0 + e;
+                v[e] = (kk < nch && row < a.d) ? reinterpret_cast<const float*>(a.C)[(int64_t)a.chunk_gen[kk] * a.d + row]
+                                               : 0.f;
+            }
+            reinterpret_cast<float4*>(a.AF)[slot * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        return;
+    }
+    if (blk * 32 >= a.d_out) return;
+    if constexpr (DT == DT_BF16) {
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kk = kk0 + e;
+            const float p = (kk < nch && row < a.d_out) ? a.P[(int64_t)kk * a.ldp + row] : 0.f;
+            const uint32_t h = f32_to_bf16(p);
+            hi[e] = (uint16_t)h;
+            lo[e] = (uint16_t)f32_to_bf16(p - __uint_as_float(h << 16));
+        }
+        const int64_t nblk = (a.d_out + 31) / 32;
+        uint4* bf = reinterpret_cast<uint4*>(a.BF);
+        bf[slot * 64 + lane] = *reinterpret_cast<uint4*>(hi);
+        bf[(nblk * a.ks_cap + slot) * 64 + lane] = *reinterpret_cast<uint4*>(lo);
+    } else {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kk = kk0 + e;
+            v[e] = (kk < nch && row < a.d_out) ? a.P[(int64_t)kk * a.ldp + row] : 0.f;
+        }
+        reinterpret_cast<float4*>(a.BF)[slot * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
 
-    f32x16 acc[2][2];
+// 4b. dW tile per wave: 32*TM rows (d) x 32*TN columns (d_out), 32x32 MFMA
+// tiles fed by contiguous fragment loads (L2-resident), no LDS and no
+// barriers; results stored as full 128-byte row pieces.
+struct GemmArgs {
+    const void* AF;
+    const void* BF;
+    int64_t ks_cap;
+    int64_t d;
+    int64_t d_out;
+    const int32_t* nchunks;
+    float* dW;
+    int64_t lddw;
+};
+
+template <int DT, int TM, int TN, bool ACC>
+__global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
+    constexpr int KB = 4;  // contraction steps whose fragments are fetched together
+    constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
+    const int lane = threadIdx.x & 63;
+    const int64_t tiles_n = (a.d_out + 32 * TN - 1) / (32 * TN);
+    const int64_t wt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t tm = wt / tiles_n, tn = wt % tiles_n;
+    const int64_t m0 = tm * 32 * TM, n0 = tn * 32 * TN;
+    if (m0 >= a.d) return;
+    const int ks_used = (*a.nchunks + 15) >> 4;
+    const int64_t mblk = (a.d + 31) / 32, nblk = (a.d_out + 31) / 32;
+    const uint4* AF = reinterpret_cast<const uint4*>(a.AF);
+    const uint4* BF = reinterpret_cast<const uint4*>(a.BF);
+    // 1 KB slot of (block, step 0, piece 0) for each fragment row block (clamped
+    // blocks past the edge are read but never stored)
+    const uint4* ab[TM];
+    const uint4* bb[TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i) ab[i] = AF + min(m0 / 32 + i, mblk - 1) * a.ks_cap * PIECES * 64 + lane;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j) bb[j] = BF + min(n0 / 32 + j, nblk - 1) * a.ks_cap * PIECES * 64 + lane;
+    const int64_t lo_off = nblk * a.ks_cap * 64;  // bf16: lo blocks follow the hi blocks
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    for (int kp = 0; kp < nch; kp += kGKP) {
-        __syncthreads();
-        // ---- A panel: sA[m][kk] = C[gen(kp+kk)][m0+m]
-        {
-            constexpr int PE = Elem<DT>::per16;
-            constexpr int MCH = kGBM / PE;        // 16-byte pieces per panel row of C
-            for (int c = t; c < kGKP * MCH; c += 256) {
-                const int kk = c % kGKP, mc = c / kGKP;
-                const int64_t m = m0 + mc * PE;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (kp + kk < nch && m < a.d) {
-                    const int gj = a.chunk_gen[kp + kk];
-                    v = load16_tail<DT>(reinterpret_cast<const char*>(a.C) + (int64_t)gj * a.d * Elem<DT>::size, m,
-                                        a.d);
-                }
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int kb = 0; kb < ks_used; kb += KB) {
+        const int nsteps = min(KB, ks_used - kb);
+        if constexpr (DT == DT_BF16) {
+            uint4 af[KB][TM], bh[KB][TN], bl[KB][TN];
 #pragma unroll
-                for (int e = 0; e < PE; ++e) {
-                    if constexpr (DT == DT_BF16)
-                        sA[(mc * PE + e) * KPAD + kk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                    else
-                        sA[(mc * PE + e) * KPAD + kk] = __uint_as_float(w[e]);
-                }
-            }
-        }
-        // ---- B panel: P[kp+kk][n0+n] -> sBh/sBl[n][kk]
-        {
-            constexpr int NCH = kGBN / 4;
-            for (int c = t; c < kGKP * NCH; c += 256) {
-                const int kk = c % kGKP, nc = c / kGKP;
-                const int64_t nn = n0 + nc * 4;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (kp + kk < nch && nn < a.d_out) {
-                    const float* src = a.P + (int64_t)(kp + kk) * a.ldp + nn;
-                    if (nn + 4 <= a.d_out) {
-                        v = *reinterpret_cast<const float4*>(src);
-                    } else {
-                        float tmp[4] = {0.f, 0.f, 0.f, 0.f};
-                        for (int e = 0; e < 4; ++e)
-                            if (nn + e < a.d_out) tmp[e] = src[e];
-                        v = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
-                    }
-                }
-                const float vv[4] = {v.x, v.y, v.z, v.w};
+            for (int st = 0; st < KB; ++st) {
+                if (st < nsteps) {
+                    const int64_t o = (int64_t)(kb + st) * 64;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (DT == DT_BF16) {
-                        const uint32_t hi = f32_to_bf16(vv[e]);
-                        const uint32_t lo = f32_to_bf16(vv[e] - __uint_as_float(hi << 16));
-                        sBh[(nc * 4 + e) * KPAD + kk] = (uint16_t)hi;
-                        sBl[(nc * 4 + e) * KPAD + kk] = (uint16_t)lo;
-                    } else {
-                        sBh[(nc * 4 + e) * KPAD + kk] = vv[e];
+                    for (int i = 0; i < TM; ++i) af[st][i] = ab[i][o];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        bh[st][j] = bb[j][o];
+                        bl[st][j] = bb[j][o + lo_off];
                     }
                 }
             }
-        }
-        __syncthreads();
-        // ---- MFMA over the panel
 #pragma unroll
-        for (int ks = 0; ks < kGKP; ks += 16) {
-            if constexpr (DT == DT_BF16) {
-                const int kq = ks + (lane >> 5) * 8;
-                bf16x8 af[2], bh[2], bl[2];
+            for (int st = 0; st < KB; ++st) {
+                if (st < nsteps) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    af[i] = *reinterpret_cast<const bf16x8*>(&sA[(wm + i * 32 + (lane & 31)) * KPAD + kq]);
-                    bh[i] = *reinterpret_cast<const bf16x8*>(&sBh[(wn + i * 32 + (lane & 31)) * KPAD + kq]);
-                    bl[i] = *reinterpret_cast<const bf16x8*>(&sBl[(wn + i * 32 + (lane & 31)) * KPAD + kq]);
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) {
+                            const bf16x8 x = __builtin_bit_cast(bf16x8, af[st][i]);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                x, __builtin_bit_cast(bf16x8, bh[st][j]), acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                x, __builtin_bit_cast(bf16x8, bl[st][j]), acc[i][j], 0, 0, 0);
+                        }
                 }
+            }
+        } else {
+            // piece h of lane group g holds chunks 16ks + 8h + 4g + 0..3;
+            // MFMA (h, e) takes element e: chunks 16ks + 8h + e and + 4
+            float4 af[KB][TM][2], bf[KB][TN][2];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bh[j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bl[j], acc[i][j], 0, 0, 0);
-                    }
-            } else {
-                // lane group (lane/32) holds chunks ks + 8*(lane/32) + 0..7; MFMA s uses element s
-                const int kq = ks + (lane >> 5) * 8;
-                float4 af[2][2], bf[2][2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
+            for (int st = 0; st < KB; ++st) {
+                if (st < nsteps) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        af[i][h] = *reinterpret_cast<const float4*>(&sA[(wm + i * 32 + (lane & 31)) * KPAD + kq + 4 * h]);
-                        bf[i][h] = *reinterpret_cast<const float4*>(&sBh[(wn + i * 32 + (lane & 31)) * KPAD + kq + 4 * h]);
+                        const int64_t o = ((int64_t)(kb + st) * 2 + h) * 64;
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) af[st][i][h] = __builtin_bit_cast(float4, ab[i][o]);
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) bf[st][j][h] = __builtin_bit_cast(float4, bb[j][o]);
                     }
+                }
+            }
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+            for (int st = 0; st < KB; ++st) {
+                if (st < nsteps) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
+                    for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][h].x, bf[j][h].x, acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][h].y, bf[j][h].y, acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][h].z, bf[j][h].z, acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][h].w, bf[j][h].w, acc[i][j], 0, 0, 0);
-                        }
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const float4 x = af[st][i][h], y = bf[st][j][h];
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc[i][j], 0, 0, 0);
+                            }
+                }
             }
         }
     }
 
-    // ---- store: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32 of a 32x32 tile
+    // element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32 of a 32x32 tile
+    const bool interior = m0 + 32 * TM <= a.d && n0 + 32 * TN <= a.d_out;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn + j * 32 + (lane & 31);
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + 32 * j + (lane & 31);
+            float* base = a.dW + (m0 + 32 * i + 4 * (lane >> 5)) * a.lddw + col;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (row < a.d && col < a.d_out) {
-                    float* p = a.dW + row * a.lddw + col;
-                    const float v = acc[i][j][e];
-                    if (a.accumulate) *p = *p + v;
-                    else __builtin_nontemporal_store(v, p);
+                const int r = 8 * (e >> 2) + (e & 3);
+                float* p = base + r * a.lddw;
+                if (interior || (m0 + 32 * i + 4 * (lane >> 5) + r < a.d && col < a.d_out)) {
+                    if constexpr (ACC) *p += acc[i][j][e];
+                    else *p = acc[i][j][e];
                 }
             }
         }
@@ -472,7 +545,7 @@ __global__ void zero_count_kernel(int32_t* c) {
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d_out) {
+WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out) {
     WgradLayout L;
     L.nb = (n + kSortBlockRows - 1) / kSortBlockRows;
     if (L.nb < 1) L.nb = 1;
@@ -488,6 +561,11 @@ WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d_out) {
     L.off_perm = off; off = align256(off + sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
     L.off_palpha = off; off = align256(off + sizeof(float) * (size_t)(n > 0 ? n : 1));
     L.off_P = off; off = align256(off + sizeof(float) * (size_t)(L.max_chunks * L.ldp));
+    // fragment-ordered product operands: 1 KB per (32-row block, 16-chunk
+    // step) for bf16 (2 KB for fp32); B holds hi and lo halves for bf16
+    L.ks_cap = (L.max_chunks + 15) / 16;
+    L.off_AT = off; off = align256(off + 2048 * (size_t)(((d + 31) / 32) * L.ks_cap));
+    L.off_BT = off; off = align256(off + 2048 * (size_t)(((d_out + 31) / 32) * L.ks_cap));
     L.total = off;
     return L;
 }
@@ -543,11 +621,26 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, st, nchunks);
     }
 
+    PrepArgs pa;
+    pa.C = a.C; pa.d = a.d; pa.d_out = a.d_out; pa.nchunks = nchunks; pa.chunk_gen = cgen; pa.P = P; pa.ldp = L.ldp;
+    pa.AF = ws + L.off_AT; pa.BF = ws + L.off_BT; pa.ks_cap = L.ks_cap;
+    {
+        constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
+        // upper bounds; the kernel trims to the real chunk count
+        const int64_t a_items = ((a.d + 31) / 32) * L.ks_cap * PIECES * 64;
+        const int64_t total = a_items + ((a.d_out + 31) / 32) * L.ks_cap * PIECES * 64;
+        hipLaunchKernelGGL(gemm_prep_kernel<DT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, pa, a_items);
+    }
     GemmArgs g;
-    g.C = a.C; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks; g.chunk_gen = cgen; g.P = P; g.ldp = L.ldp;
-    g.dW = a.dW; g.lddw = a.lddw; g.accumulate = a.accumulate;
-    dim3 grid((unsigned)((a.d_out + kGBN - 1) / kGBN), (unsigned)((a.d + kGBM - 1) / kGBM));
-    hipLaunchKernelGGL(gen_gemm_kernel<DT>, grid, dim3(256), 0, st, g);
+    g.AF = pa.AF; g.BF = pa.BF; g.ks_cap = L.ks_cap; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks;
+    g.dW = a.dW; g.lddw = a.lddw;
+    const int64_t waves = ((a.d + 32 * PAMM_GEMM_TM - 1) / (32 * PAMM_GEMM_TM)) *
+                          ((a.d_out + 32 * PAMM_GEMM_TN - 1) / (32 * PAMM_GEMM_TN));
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (a.accumulate)
+        hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, true>), grid, dim3(256), 0, st, g);
+    else
+        hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, false>), grid, dim3(256), 0, st, g);
     return hipGetLastError();
 }
 
