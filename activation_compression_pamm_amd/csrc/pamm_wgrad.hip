@@ -31,6 +31,13 @@
 #include "pamm_device.hpp"
 #include "pamm_kernels.hpp"
 
+// segmented reduction: lanes per row piece, rows in flight per row group
+#ifndef PAMM_SR_LPR
+#define PAMM_SR_LPR 8
+#endif
+#ifndef PAMM_SR_U
+#define PAMM_SR_U 8
+#endif
 // dW tile of one wave: 32*TM rows x 32*TN columns
 #ifndef PAMM_GEMM_TM
 #define PAMM_GEMM_TM 2
@@ -250,30 +257,33 @@ struct ScatterArgs {
     int64_t ldp;
 };
 
-template <int DT>
+// One wave per (chunk, column slab): LPR lanes cover one row piece of
+// 16*LPR bytes (whole 128-byte lines), 64/LPR row groups walk the chunk's
+// rows, U rows per group in flight.
+template <int DT, int LPR, int U>
 __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
     constexpr int PE = Elem<DT>::per16;   // elements per lane
-    constexpr int SC = 8 * PE;            // columns per slab (128 bytes)
-    constexpr int U = 8;                  // rows in flight per lane group
+    constexpr int SC = LPR * PE;          // columns per slab
+    constexpr int RG = 64 / LPR;          // row groups per wave
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 3, l8 = lane & 7;
+    const int g = lane / LPR, lq = lane % LPR;
     const int64_t nitems = (int64_t)(*a.nchunks) * a.nslab;
     const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
     for (int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); item < nitems;
          item += wstride) {
         const int64_t ch = item / a.nslab;
-        const int64_t col = (item % a.nslab) * SC + l8 * PE;
+        const int64_t col = (item % a.nslab) * SC + lq * PE;
         const int begin = a.chunk_begin[ch];
         const int cnt = a.chunk_count[ch];
         float acc[PE];
 #pragma unroll
         for (int e = 0; e < PE; ++e) acc[e] = 0.f;
-        for (int t0 = g; t0 < cnt; t0 += 8 * U) {
+        for (int t0 = g; t0 < cnt; t0 += RG * U) {
             int ii[U];
             float aa[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int tt = t0 + 8 * u;
+                const int tt = t0 + RG * u;
                 ii[u] = tt < cnt ? a.perm[begin + tt] : -1;
                 aa[u] = tt < cnt ? a.palpha[begin + tt] : 0.f;
             }
@@ -290,9 +300,9 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
                 for (int e = 0; e < PE; ++e) acc[e] = __builtin_fmaf(aa[u], v[e], acc[e]);
             }
         }
-        // fixed-order combine of the 8 row groups
+        // fixed-order combine of the row groups
 #pragma unroll
-        for (int m = 8; m < 64; m <<= 1)
+        for (int m = LPR; m < 64; m <<= 1)
 #pragma unroll
             for (int e = 0; e < PE; ++e) acc[e] += shfl_xor(acc[e], m);
         if (g == 0) {
@@ -606,7 +616,7 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         r.dY = reinterpret_cast<const char*>(a.dY);
         r.lddy_bytes = a.lddy_bytes;
         r.d_out = a.d_out;
-        constexpr int SC = 8 * Elem<DT>::per16;
+        constexpr int SC = PAMM_SR_LPR * Elem<DT>::per16;
         r.nslab = (a.d_out + SC - 1) / SC;
         r.nchunks = nchunks; r.chunk_begin = cbeg; r.chunk_count = ccnt; r.perm = perm; r.palpha = palpha;
         r.P = P; r.ldp = L.ldp;
@@ -615,7 +625,7 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 8;
         if (grid > cap) grid = cap;
         if (grid < 1) grid = 1;
-        hipLaunchKernelGGL(scatter_reduce_kernel<DT>, dim3((unsigned)grid), dim3(256), 0, st, r);
+        hipLaunchKernelGGL((scatter_reduce_kernel<DT, PAMM_SR_LPR, PAMM_SR_U>), dim3((unsigned)grid), dim3(256), 0, st, r);
     } else {
         // no generators or no rows: no chunks, dW = 0 (or unchanged when accumulating)
         hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, st, nchunks);

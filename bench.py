@@ -43,7 +43,23 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle's timed sample")
     p.add_argument("--cpu-cols", type=int, default=6144, help="dW columns of the oracle's timed sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (known bytes) to scale memory counters")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch.
+    Profiling it with the FETCH_SIZE / WRITE_SIZE counters gives the factor
+    that turns those counters into bytes."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4, "copy_calibration_bytes_written": dst.numel() * 4,
+                      "launches": 3}))
 
 
 def algorithmic(p, kept):
@@ -95,6 +111,9 @@ def cpu_baseline(X, dY, gen_idx, p, rows, cols):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -155,6 +174,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
+    t_submit = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
@@ -199,6 +219,7 @@ def main():
             "wgrad_alg_gbs": round((rb + pb) / (t_wgrad * 1e-3) / 1e9, 1),
             "kept_fraction": round(kept, 4),
             "host_sampling_us": round(t_sample * 1e6, 2),
+            "host_submit_us_per_step": round(t_submit * 1e6 / args.steps, 2),
         },
     }
     if not args.no_cpu_baseline:
