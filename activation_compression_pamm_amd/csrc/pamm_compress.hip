@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
         int64_t off = (int64_t)stage_of(s) * RB + q8 * 16;
         off = off >= a.row_bytes ? -(int64_t)q8 * 16 : (int64_t)stage_of(s) * RB;  // chunk past the row end: chunk 0
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) xr[U][i] = *reinterpret_cast<const uint4*>(xsrc[i] + off);
+        for (int i = 0; i < XPT; ++i) xr[U][i] = load16_nt(xsrc[i] + off);  // X is read once: non-temporal
 #pragma unroll
         for (int i = 0; i < CPT; ++i) cr[U][i] = *reinterpret_cast<const uint4*>(csrc[i] + off);
     };

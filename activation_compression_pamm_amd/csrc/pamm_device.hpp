@@ -78,6 +78,14 @@ __device__ __forceinline__ uint4 load16_tail(const char* row, int64_t col, int64
     return v;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint (streamed data that is not reused).
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 template <typename T>

@@ -290,8 +290,11 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
             uint4 vv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                vv[u] = ii[u] >= 0 ? load16_tail<DT>(a.dY + (int64_t)ii[u] * a.lddy_bytes, col, a.d_out)
-                                   : make_uint4(0, 0, 0, 0);
+            // dY rows are read once: non-temporal loads for whole 16-byte groups
+                vv[u] = ii[u] < 0 ? make_uint4(0, 0, 0, 0)
+                        : (col + PE <= a.d_out
+                               ? load16_nt(a.dY + (int64_t)ii[u] * a.lddy_bytes + col * Elem<DT>::size)
+                               : load16_tail<DT>(a.dY + (int64_t)ii[u] * a.lddy_bytes, col, a.d_out));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float v[PE];
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(PrepArgs a, int64_t a_it
 
 // 4b. dW tile per wave: 32*TM rows (d) x 32*TN columns (d_out), 32x32 MFMA
 // tiles fed by contiguous fragment loads (L2-resident), no LDS and no
-// barriers; results stored as full 128-byte row pieces.
+// barriers; results stored (non-temporal) as full 128-byte row pieces.
 struct GemmArgs {
     const void* AF;
     const void* BF;
@@ -539,8 +542,11 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
                 const int r = 8 * (e >> 2) + (e & 3);
                 float* p = base + r * a.lddw;
                 if (interior || (m0 + 32 * i + 4 * (lane >> 5) + r < a.d && col < a.d_out)) {
-                    if constexpr (ACC) *p += acc[i][j][e];
-                    else *p = acc[i][j][e];
+                    // non-temporal: dW goes straight to HBM instead of parking
+                    // ~200 MB of dirty lines in the memory-side cache, whose
+                    // write-back would otherwise slow the next kernel
+                    const float v = ACC ? *p + acc[i][j][e] : acc[i][j][e];
+                    __builtin_nontemporal_store(v, p);
                 }
             }
         }
