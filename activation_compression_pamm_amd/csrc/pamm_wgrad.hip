@@ -146,6 +146,18 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int64_t b = blockIdx.x;
 
+    // this thread's rows: issue their f and alpha loads first so they overlap
+    // the histogram reads below
+    const int64_t r0 = b * kSortBlockRows + wave * 256;
+    int fv[4];
+    float av[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+        const int64_t i = r0 + sub * 64 + lane;
+        fv[sub] = i < a.n ? a.f[i] : -1;
+        av[sub] = i < a.n ? a.alpha[i] : 0.f;
+    }
+
     // segment sizes and the rows of each generator that precede this block:
     // the whole histogram is read with coalesced, independent loads and
     // summed with LDS integer atomics (exact, so the order does not matter)
@@ -200,13 +212,10 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     __syncthreads();
 
     // per-wave counts over the wave's 256 rows
-    const int64_t r0 = b * kSortBlockRows + wave * 256;
-    int fv[4];
     bool ok[4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-        const int64_t i = r0 + sub * 64 + lane;
-        const int fi = i < a.n ? a.f[i] : -1;
+        const int fi = fv[sub];
         ok[sub] = fi >= 0 && fi < k;
         fv[sub] = ok[sub] ? fi : 0;
         if (ok[sub]) atomicAdd(&s_w[wave * k + fi], 1);
@@ -232,7 +241,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
             const int rank = __popcll(m & lanemask_lt());
             const int pos = s_w[wave * k + fv[sub]] + rank;
             a.perm[pos] = (int32_t)i;
-            a.palpha[pos] = a.alpha[i];
+            a.palpha[pos] = av[sub];
         }
         // all lanes have read the running position; the lowest lane of each
         // group advances it (LDS accesses of one wave stay in program order)
