@@ -439,7 +439,7 @@ struct GemmArgs {
 
 template <int DT, int TM, int TN, bool ACC>
 __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
-    constexpr int KB = 4;  // contraction steps whose fragments are fetched together
+    constexpr int KB = 1;  // contraction steps whose fragments are fetched together (measured best)
     constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
     const int lane = threadIdx.x & 63;
     const int64_t tiles_n = (a.d_out + 32 * TN - 1) / (32 * TN);
