@@ -162,11 +162,10 @@ __device__ __forceinline__ void epilogue_rows(const CompressArgs& a, const f32x4
 
 // The compress kernel (see the file comment).  WM rows per wave, NW waves,
 // KN generators per tile, PD stages of register prefetch.
-template <int DT, int WM, int NW, int KN, int PD>
+template <int DT, int WM, int NW, int KN, int PD, int RB>
 __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
-    constexpr int RB = 128;                           // bytes of each row per stage
-    constexpr int SUBS = RB / 64;
-    constexpr int CH = RB / 16;                       // 8 chunks per row
+    constexpr int SUBS = RB / 64;                     // MFMA K sub-steps per stage
+    constexpr int CH = RB / 16;                       // 16-byte chunks per staged row
     constexpr int RPI = 64 / CH;                      // rows per wave-wide load
     constexpr int BM = WM * NW;
     constexpr int MT = WM / 16;
@@ -178,6 +177,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     constexpr int E = RB / Elem<DT>::size;
     constexpr int P = Elem<DT>::per16;
     static_assert(BM % (RPI * NW) == 0 && PD % 2 == 0 && PD >= 2, "tile shape");
+    static_assert(RB == 128 || RB == 256 || RB == 512, "stage width");
 
     __shared__ __align__(16) char s_x0[BM * RB];
     __shared__ __align__(16) char s_x1[BM * RB];
@@ -222,29 +222,29 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
         }
     }
 
-    // ---- rows this lane fetches: load i covers tile rows RPI*(wave + NW*i) + lane/8,
-    // 16-byte chunk lane%8 of each 128-byte stage
-    const int q8 = lane & 7;
+    // ---- rows this lane fetches: load i covers tile rows RPI*(wave + NW*i) + lane/CH,
+    // 16-byte chunk lane%CH of each RB-byte stage
+    const int qc = lane % CH;
     const char* xsrc[XPT];
     int xdst[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int r = RPI * (wave + NW * i) + (lane >> 3);
+        const int r = RPI * (wave + NW * i) + lane / CH;
         int64_t g = m0 + r;
         if (g >= a.n) g = a.n - 1;  // padding rows: any valid row, results unused
-        xsrc[i] = X + g * a.ldx_bytes + q8 * 16;
-        xdst[i] = swz<RB>(r, q8);
+        xsrc[i] = X + g * a.ldx_bytes + qc * 16;
+        xdst[i] = swz<RB>(r, qc);
     }
     const char* csrc[CPT];
     int cdst[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-        const int r = RPI * (wave + NW * i) + (lane >> 3);
+        const int r = RPI * (wave + NW * i) + lane / CH;
         const int jj = min(r, max(ktile - 1, 0));  // padding generators: any valid one, masked later
         int64_t g = a.k > 0 ? a.gen_idx[gen0 + jj] : 0;
         g = g < 0 ? 0 : (g >= a.n ? a.n - 1 : g);
-        csrc[i] = X + g * a.ldx_bytes + q8 * 16;
-        cdst[i] = swz<RB>(r, q8);
+        csrc[i] = X + g * a.ldx_bytes + qc * 16;
+        cdst[i] = swz<RB>(r, qc);
     }
     // rotated stage order (workgroups start at different column ranges);
     // padding stages past the end map to the last stage and are zeroed
@@ -255,8 +255,8 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     uint4 xr[PD][XPT], cr[PD][CPT];
     auto issue = [&](int s, auto slotc) {
         constexpr int U = decltype(slotc)::value;
-        int64_t off = (int64_t)stage_of(s) * RB + q8 * 16;
-        off = off >= a.row_bytes ? -(int64_t)q8 * 16 : (int64_t)stage_of(s) * RB;  // chunk past the row end: chunk 0
+        int64_t off = (int64_t)stage_of(s) * RB + qc * 16;
+        off = off >= a.row_bytes ? -(int64_t)qc * 16 : (int64_t)stage_of(s) * RB;  // chunk past the row end: chunk 0
 #pragma unroll
         for (int i = 0; i < XPT; ++i) xr[U][i] = load16_nt(xsrc[i] + off);  // X is read once: non-temporal
 #pragma unroll
@@ -303,9 +303,9 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
             for (int i = 0; i < CPT; ++i) cw[i] = cr[U][i];
             if (lim < E) {  // uniform: the last real stage and the padding stages
 #pragma unroll
-                for (int i = 0; i < XPT; ++i) mask_chunk(xw[i], q8 * P, lim);
+                for (int i = 0; i < XPT; ++i) mask_chunk(xw[i], qc * P, lim);
 #pragma unroll
-                for (int i = 0; i < CPT; ++i) mask_chunk(cw[i], q8 * P, lim);
+                for (int i = 0; i < CPT; ++i) mask_chunk(cw[i], qc * P, lim);
             }
 #pragma unroll
             for (int i = 0; i < XPT; ++i) *reinterpret_cast<uint4*>(sx + xdst[i]) = xw[i];
@@ -393,30 +393,30 @@ __global__ __launch_bounds__(256) void compress_empty_kernel(int64_t n, int32_t*
     if (row < n) { f[row] = -1; alpha[row] = 0.f; }
 }
 
-template <int DT, int WM, int NW, int KN, int PD>
+template <int DT, int WM, int NW, int KN, int PD, int RB>
 static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStream_t st) {
     constexpr int BM = WM * NW;
     dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)ntiles);
-    hipLaunchKernelGGL((compress_rs_kernel<DT, WM, NW, KN, PD>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((compress_rs_kernel<DT, WM, NW, KN, PD, RB>), grid, dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
 
 // Tile shapes per generator-tile width: rows per wave, waves, generators,
-// register prefetch depth (stages).
+// register prefetch depth (stages), bytes of each row per stage.
 #ifndef PAMM_COMPRESS_RS16
-#define PAMM_COMPRESS_RS16 16, 8, 16, 4
+#define PAMM_COMPRESS_RS16 16, 8, 16, 4, 128
 #endif
 #ifndef PAMM_COMPRESS_RS32
-#define PAMM_COMPRESS_RS32 16, 8, 32, 4
+#define PAMM_COMPRESS_RS32 16, 8, 32, 4, 128
 #endif
 #ifndef PAMM_COMPRESS_RS64
-#define PAMM_COMPRESS_RS64 16, 8, 64, 4
+#define PAMM_COMPRESS_RS64 16, 8, 64, 4, 128
 #endif
 #ifndef PAMM_COMPRESS_RS128
-#define PAMM_COMPRESS_RS128 16, 8, 128, 4
+#define PAMM_COMPRESS_RS128 16, 8, 128, 4, 128
 #endif
 #ifndef PAMM_COMPRESS_RS256
-#define PAMM_COMPRESS_RS256 16, 8, 256, 4
+#define PAMM_COMPRESS_RS256 16, 8, 256, 4, 128
 #endif
 
 template <int DT>
