@@ -45,8 +45,7 @@ struct WgradLayout {
     int64_t nb;         // sort blocks
     int64_t max_chunks; // upper bound on row chunks
     size_t off_hist, off_seg, off_nchunks, off_chunk_gen, off_chunk_begin, off_chunk_count;
-    size_t off_perm, off_palpha, off_P, off_AT, off_BT;
-    int64_t ldp;        // row stride of the chunk partial sums P (floats)
+    size_t off_perm, off_palpha, off_AT, off_BT;
     int64_t ks_cap;     // 16-chunk contraction steps the product operands hold
     size_t total;
 };

@@ -14,16 +14,19 @@
 //                      with wave ballots and writes (row, alpha) in generator
 //                      order; block 0 also cuts each generator's rows into
 //                      chunks of at most kChunkRows rows.
-//   3. scatter_reduce  one wave per (chunk, 128-byte column slab): sums
+//   3. scatter_reduce  gathers the product's A operand (each chunk's
+//                      generator row of C, in MFMA fragment order), then
+//                      one wave per (chunk, 128-byte column slab): sums
 //                      alpha_i * dY[i, slab] over the chunk's rows, reading
-//                      only kept rows, each 128-byte row piece by 8 lanes;
-//                      writes the chunk's partial row P[chunk, slab] (fp32).
+//                      only kept rows, each 128-byte row piece by 8 lanes,
+//                      and writes the chunk's partial row P[chunk, slab]
+//                      (fp32) straight into the product's B operand.
 //                      Fixed summation order, no atomics: deterministic.
 //   4. gen_gemm        dW = sum over chunks of c_gen(chunk) (x) P[chunk],
 //                      i.e. C^T B~ with B~ split into its chunk partials.
-//                      MFMA 32x32 tiles fed from LDS panels that are stored
-//                      transposed (contraction index contiguous); bf16 uses
-//                      a hi/lo bf16 split of P, fp32 uses fp32 MFMA.
+//                      MFMA 32x32 tiles fed by contiguous fragment loads,
+//                      no LDS; bf16 uses a hi/lo bf16 split of P, fp32 uses
+//                      fp32 MFMA.
 // Dropped rows (f outside [0, k)) are never sorted, so their dY rows are not
 // read at all.
 #include <type_traits>
@@ -43,7 +46,11 @@
 #define PAMM_GEMM_TM 2
 #endif
 #ifndef PAMM_GEMM_TN
-#define PAMM_GEMM_TN 2
+#define PAMM_GEMM_TN 1
+#endif
+// contraction steps (16 chunks each) whose fragments a wave fetches together
+#ifndef PAMM_GEMM_KB
+#define PAMM_GEMM_KB 1
 #endif
 
 namespace pamm {
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
 
     // block 0 cuts every generator's rows into chunks (before s_tot becomes starts)
     if (b == 0) {
-        int* s_nch = s_w;  // reuse: per-generator chunk count -> chunk offset
+        int* s_nch = s_w;  // reuse: per-generator chunk count -> first chunk
         for (int j = t; j < k; j += 256) s_nch[j] = (s_tot[j] + kChunkRows - 1) / kChunkRows;
         __syncthreads();
         const int total_chunks = block_exclusive_scan(s_nch, k, s_tmp);
@@ -262,13 +269,51 @@ struct ScatterArgs {
     const int32_t* chunk_count;
     const int32_t* perm;
     const float* palpha;
-    float* P;
-    int64_t ldp;
+    const int32_t* chunk_gen;
+    const void* C;    // [k x d]
+    int64_t d;
+    void* AF;         // product operand A, MFMA-fragment order
+    void* BF;         // product operand B, MFMA-fragment order
+    int64_t ks_cap;   // contraction steps BF holds
+    int64_t ncols;    // columns BF holds: d_out rounded up to 32
 };
 
-// One wave per (chunk, column slab): LPR lanes cover one row piece of
-// 16*LPR bytes (whole 128-byte lines), 64/LPR row groups walk the chunk's
-// rows, U rows per group in flight.
+// The product's operands are stored in MFMA-fragment order, so that every
+// fragment a wave of gen_gemm needs is one contiguous 1 KB (64 lanes x 16
+// bytes) load.  For 32-row block mb (rows of dW, i.e. d) or 32-column block
+// nb (d_out) and contraction step ks (16 chunks):
+//   bf16: lane l, piece 0:  A[32mb + l%32][16ks + 8(l/32) + 0..7]
+//   fp32: lane l, piece h:  A[32mb + l%32][16ks + 8h + 4(l/32) + 0..3]
+// with A[m][kk] = C[gen(kk)][m] and B[n][kk] = P[kk][n] (bf16: P split into
+// hi + lo bf16 terms, B holding all hi blocks, then all lo blocks); entries
+// past d or the chunk count are zero.
+//
+// One A slot (1 KB) per wave: lane l gathers its 16 bytes from C.
+template <int DT>
+__device__ __forceinline__ void write_a_slot(const ScatterArgs& a, int64_t slot, int ks_used, int nch, int lane) {
+    constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
+    typedef typename std::conditional<DT == DT_BF16, uint16_t, float>::type T;
+    constexpr int PE = 16 / (int)sizeof(T);
+    const int piece = (int)(slot % PIECES);
+    const int64_t ks = (slot / PIECES) % ks_used;
+    const int64_t mb = (slot / PIECES) / ks_used;
+    const int64_t m = mb * 32 + (lane & 31);
+    const int kk0 = (int)(ks * 16) + (DT == DT_BF16 ? 8 * (lane >> 5) : 8 * piece + 4 * (lane >> 5));
+    const T* C = reinterpret_cast<const T*>(a.C);
+    T v[PE];
+#pragma unroll
+    for (int e = 0; e < PE; ++e) {
+        const int kk = kk0 + e;
+        v[e] = (kk < nch && m < a.d) ? C[(int64_t)a.chunk_gen[kk] * a.d + m] : T(0);
+    }
+    reinterpret_cast<uint4*>(a.AF)[((mb * a.ks_cap + ks) * PIECES + piece) * 64 + lane] =
+        *reinterpret_cast<uint4*>(v);
+}
+
+// Items: first the A slots, then one per (chunk, column slab).  For the
+// latter LPR lanes cover one row piece of 16*LPR bytes (whole 128-byte
+// lines), 64/LPR row groups walk the chunk's rows, U rows per group in
+// flight.
 template <int DT, int LPR, int U>
 __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
     constexpr int PE = Elem<DT>::per16;   // elements per lane
@@ -276,14 +321,23 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
     constexpr int RG = 64 / LPR;          // row groups per wave
     const int lane = threadIdx.x & 63;
     const int g = lane / LPR, lq = lane % LPR;
-    const int64_t nitems = (int64_t)(*a.nchunks) * a.nslab;
+    // chunks up to the next multiple of 16 are written too (as zeros), so
+    // the product's last contraction step holds no stale workspace
+    const int nch = *a.nchunks;
+    const int ks_used = (nch + 15) >> 4;
+    const int64_t a_slots = (a.d + 31) / 32 * ks_used * (DT == DT_BF16 ? 1 : 2);
+    const int64_t nitems = a_slots + (int64_t)ks_used * 16 * a.nslab;
     const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
     for (int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); item < nitems;
          item += wstride) {
-        const int64_t ch = item / a.nslab;
-        const int64_t col = (item % a.nslab) * SC + lq * PE;
-        const int begin = a.chunk_begin[ch];
-        const int cnt = a.chunk_count[ch];
+        if (item < a_slots) {
+            write_a_slot<DT>(a, item, ks_used, nch, lane);
+            continue;
+        }
+        const int64_t ch = (item - a_slots) / a.nslab;
+        const int64_t col = ((item - a_slots) % a.nslab) * SC + lq * PE;
+        const int begin = ch < nch ? a.chunk_begin[ch] : 0;
+        const int cnt = ch < nch ? a.chunk_count[ch] : 0;
         float acc[PE];
 #pragma unroll
         for (int e = 0; e < PE; ++e) acc[e] = 0.f;
@@ -317,15 +371,32 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
         for (int m = LPR; m < 64; m <<= 1)
 #pragma unroll
             for (int e = 0; e < PE; ++e) acc[e] += shfl_xor(acc[e], m);
-        if (g == 0) {
-            float* dst = a.P + ch * a.ldp + col;
-            if (col + PE <= a.d_out) {
+        // every lane now holds the sums of its PE columns; lane g of the
+        // group stores column g of them straight into the B fragments
+        // (B[n][kk] = P[kk][n]): bf16 lane l, piece 0 holds
+        // B[32nb + l%32][16ks + 8(l/32) + 0..7], split into a hi and a lo
+        // bf16 term (lo blocks after all hi blocks); fp32 lane l, piece h
+        // holds B[32nb + l%32][16ks + 8h + 4(l/32) + 0..3]
+        if (g < PE) {
+            float v = acc[0];
 #pragma unroll
-                for (int e = 0; e < PE; e += 4)
-                    *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-            } else {
-                for (int e = 0; e < PE; ++e)
-                    if (col + e < a.d_out) dst[e] = acc[e];
+            for (int e = 1; e < PE; ++e) v = g == e ? acc[e] : v;
+            const int64_t n = col + g;
+            if (n < a.ncols) {
+                const int64_t nb = n >> 5, ks = ch >> 4;
+                const int nl = (int)(n & 31), c16 = (int)(ch & 15);
+                if constexpr (DT == DT_BF16) {
+                    const int64_t idx = ((nb * a.ks_cap + ks) * 64 + nl + 32 * (c16 >> 3)) * 8 + (c16 & 7);
+                    const uint32_t hi = f32_to_bf16(v);
+                    const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
+                    uint16_t* bf = reinterpret_cast<uint16_t*>(a.BF);
+                    bf[idx] = (uint16_t)hi;
+                    bf[idx + (a.ncols >> 5) * a.ks_cap * 64 * 8] = (uint16_t)lo;
+                } else {
+                    const int64_t idx =
+                        (((nb * a.ks_cap + ks) * 2 + (c16 >> 3)) * 64 + nl + 32 * ((c16 >> 2) & 1)) * 4 + (c16 & 3);
+                    reinterpret_cast<float*>(a.BF)[idx] = v;
+                }
             }
         }
     }
@@ -334,96 +405,7 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
 // ---------------------------------------------------------------------------
 // 4. generator product dW = sum_chunk c_gen(chunk) (x) P[chunk]
 // ---------------------------------------------------------------------------
-// 4a. Operands stored in MFMA-fragment order, so that every fragment a wave
-// needs is one contiguous 1 KB (64 lanes x 16 bytes) load.  For 32-row block
-// mb (rows of dW, i.e. d) or 32-column block nb (d_out) and contraction step
-// ks (16 chunks):
-//   bf16: lane l, piece 0:  A[32mb + l%32][16ks + 8(l/32) + 0..7]
-//   fp32: lane l, piece h:  A[32mb + l%32][16ks + 8h + 4(l/32) + 0..3]
-// with A[m][kk] = C[gen(kk)][m] and B[n][kk] = P[kk][n] (bf16: P split into
-// hi + lo bf16 terms, B holding all hi blocks, then all lo blocks); entries
-// past d, d_out or the chunk count are zero.
-struct PrepArgs {
-    const void* C;
-    int64_t d;
-    int64_t d_out;
-    const int32_t* nchunks;
-    const int32_t* chunk_gen;
-    const float* P;
-    int64_t ldp;
-    void* AF;       // A fragments
-    void* BF;       // B fragments
-    int64_t ks_cap; // contraction steps the buffers hold
-};
-
-template <int DT>
-__global__ __launch_bounds__(256) void gemm_prep_kernel(PrepArgs a, int64_t a_items) {
-    constexpr int PIECES = DT == DT_BF16 ? 1 : 2;    // 16-byte pieces per lane per step
-    const int nch = *a.nchunks;
-    const int ks_used = (nch + 15) >> 4;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    // idx -> (block, step, piece, lane); lane fastest so stores are contiguous
-    const bool is_a = idx < a_items;
-    const int64_t j = is_a ? idx : idx - a_items;
-    const int lane = (int)(j & 63);
-    const int64_t rest = j >> 6;
-    const int piece = (int)(rest % PIECES);
-    const int64_t ks = (rest / PIECES) % a.ks_cap;
-    const int64_t blk = (rest / PIECES) / a.ks_cap;
-    if (ks >= ks_used) return;
-    const int64_t row = blk * 32 + (lane & 31);   // m (A) or n (B)
-    const int kk0 = (int)(ks * 16) + (DT == DT_BF16 ? 8 * (lane >> 5) : 8 * piece + 4 * (lane >> 5));
-    const int64_t slot = (blk * a.ks_cap + ks) * PIECES + piece;   // 1 KB slot index
-    if (is_a) {
-        if (blk * 32 >= a.d) return;
-        if constexpr (DT == DT_BF16) {
-            uint16_t v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kk = kk0 + e;
-                v[e] = (kk < nch && row < a.d)
-                           ? reinterpret_cast<const uint16_t*>(a.C)[(int64_t)a.chunk_gen[kk] * a.d + row] : (uint16_t)0;
-            }
-            reinterpret_cast<uint4*>(a.AF)[slot * 64 + lane] = *reinterpret_cast<uint4*>(v);
-        } else {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kk = kk0 + e;
-                v[e] = (kk < nch && row < a.d) ? reinterpret_cast<const float*>(a.C)[(int64_t)a.chunk_gen[kk] * a.d + row]
-                                               : 0.f;
-            }
-            reinterpret_cast<float4*>(a.AF)[slot * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
-        }
-        return;
-    }
-    if (blk * 32 >= a.d_out) return;
-    if constexpr (DT == DT_BF16) {
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int kk = kk0 + e;
-            const float p = (kk < nch && row < a.d_out) ? a.P[(int64_t)kk * a.ldp + row] : 0.f;
-            const uint32_t h = f32_to_bf16(p);
-            hi[e] = (uint16_t)h;
-            lo[e] = (uint16_t)f32_to_bf16(p - __uint_as_float(h << 16));
-        }
-        const int64_t nblk = (a.d_out + 31) / 32;
-        uint4* bf = reinterpret_cast<uint4*>(a.BF);
-        bf[slot * 64 + lane] = *reinterpret_cast<uint4*>(hi);
-        bf[(nblk * a.ks_cap + slot) * 64 + lane] = *reinterpret_cast<uint4*>(lo);
-    } else {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int kk = kk0 + e;
-            v[e] = (kk < nch && row < a.d_out) ? a.P[(int64_t)kk * a.ldp + row] : 0.f;
-        }
-        reinterpret_cast<float4*>(a.BF)[slot * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
-    }
-}
-
-// 4b. dW tile per wave: 32*TM rows (d) x 32*TN columns (d_out), 32x32 MFMA
+// 4. dW tile per wave: 32*TM rows (d) x 32*TN columns (d_out), 32x32 MFMA
 // tiles fed by contiguous fragment loads (L2-resident), no LDS and no
 // barriers; results stored (non-temporal) as full 128-byte row pieces.
 struct GemmArgs {
@@ -439,7 +421,7 @@ struct GemmArgs {
 
 template <int DT, int TM, int TN, bool ACC>
 __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
-    constexpr int KB = 1;  // contraction steps whose fragments are fetched together (measured best)
+    constexpr int KB = PAMM_GEMM_KB;  // contraction steps whose fragments are fetched together
     constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
     const int lane = threadIdx.x & 63;
     const int64_t tiles_n = (a.d_out + 32 * TN - 1) / (32 * TN);
@@ -575,7 +557,6 @@ WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out) {
     L.nb = (n + kSortBlockRows - 1) / kSortBlockRows;
     if (L.nb < 1) L.nb = 1;
     L.max_chunks = (n + kChunkRows - 1) / kChunkRows + k;
-    L.ldp = (d_out + 7) & ~(int64_t)7;
     size_t off = 0;
     L.off_hist = off; off = align256(off + sizeof(int32_t) * (size_t)(L.nb * (k > 0 ? k : 1)));
     L.off_seg = off; off = align256(off + sizeof(int32_t) * (size_t)(k + 1));
@@ -585,7 +566,6 @@ WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out) {
     L.off_chunk_count = off; off = align256(off + sizeof(int32_t) * (size_t)L.max_chunks);
     L.off_perm = off; off = align256(off + sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
     L.off_palpha = off; off = align256(off + sizeof(float) * (size_t)(n > 0 ? n : 1));
-    L.off_P = off; off = align256(off + sizeof(float) * (size_t)(L.max_chunks * L.ldp));
     // fragment-ordered product operands: 1 KB per (32-row block, 16-chunk
     // step) for bf16 (2 KB for fp32); B holds hi and lo halves for bf16
     L.ks_cap = (L.max_chunks + 15) / 16;
@@ -607,7 +587,6 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     int32_t* ccnt = reinterpret_cast<int32_t*>(ws + L.off_chunk_count);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.off_perm);
     float* palpha = reinterpret_cast<float*>(ws + L.off_palpha);
-    float* P = reinterpret_cast<float*>(ws + L.off_P);
     const int k = a.k;
 
     if (k > 0 && a.n > 0) {
@@ -634,8 +613,9 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         constexpr int SC = PAMM_SR_LPR * Elem<DT>::per16;
         r.nslab = (a.d_out + SC - 1) / SC;
         r.nchunks = nchunks; r.chunk_begin = cbeg; r.chunk_count = ccnt; r.perm = perm; r.palpha = palpha;
-        r.P = P; r.ldp = L.ldp;
-        const int64_t max_items = L.max_chunks * r.nslab;
+        r.chunk_gen = cgen; r.C = a.C; r.d = a.d; r.AF = ws + L.off_AT;
+        r.BF = ws + L.off_BT; r.ks_cap = L.ks_cap; r.ncols = (a.d_out + 31) & ~(int64_t)31;
+        const int64_t max_items = (a.d + 31) / 32 * L.ks_cap * 2 + L.ks_cap * 16 * r.nslab;
         int64_t grid = (max_items + 3) / 4;
         const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 8;
         if (grid > cap) grid = cap;
@@ -646,18 +626,8 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, st, nchunks);
     }
 
-    PrepArgs pa;
-    pa.C = a.C; pa.d = a.d; pa.d_out = a.d_out; pa.nchunks = nchunks; pa.chunk_gen = cgen; pa.P = P; pa.ldp = L.ldp;
-    pa.AF = ws + L.off_AT; pa.BF = ws + L.off_BT; pa.ks_cap = L.ks_cap;
-    {
-        constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
-        // upper bounds; the kernel trims to the real chunk count
-        const int64_t a_items = ((a.d + 31) / 32) * L.ks_cap * PIECES * 64;
-        const int64_t total = a_items + ((a.d_out + 31) / 32) * L.ks_cap * PIECES * 64;
-        hipLaunchKernelGGL(gemm_prep_kernel<DT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, pa, a_items);
-    }
     GemmArgs g;
-    g.AF = pa.AF; g.BF = pa.BF; g.ks_cap = L.ks_cap; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks;
+    g.AF = ws + L.off_AT; g.BF = ws + L.off_BT; g.ks_cap = L.ks_cap; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks;
     g.dW = a.dW; g.lddw = a.lddw;
     const int64_t waves = ((a.d + 32 * PAMM_GEMM_TM - 1) / (32 * PAMM_GEMM_TM)) *
                           ((a.d_out + 32 * PAMM_GEMM_TN - 1) / (32 * PAMM_GEMM_TN));
