@@ -48,10 +48,6 @@
 #ifndef PAMM_GEMM_TN
 #define PAMM_GEMM_TN 1
 #endif
-// contraction steps (16 chunks each) whose fragments a wave fetches together
-#ifndef PAMM_GEMM_KB
-#define PAMM_GEMM_KB 1
-#endif
 
 namespace pamm {
 
@@ -70,6 +66,11 @@ __device__ __forceinline__ uint64_t match_lanes(int v, bool valid, int nbits) {
     }
     return m;
 }
+
+// Compiler-only memory barrier: loads issued before it stay before it (the
+// compiler would otherwise sink a prefetch into the iteration that uses it);
+// it emits no instruction and no wait.
+__device__ __forceinline__ void pin_issued_loads() { asm volatile("" ::: "memory"); }
 
 // Exclusive prefix sum over s[0..len) in LDS with a 256-thread block; returns
 // the total.  `tmp` needs 256 ints of LDS.
@@ -421,7 +422,6 @@ struct GemmArgs {
 
 template <int DT, int TM, int TN, bool ACC>
 __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
-    constexpr int KB = PAMM_GEMM_KB;  // contraction steps whose fragments are fetched together
     constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
     const int lane = threadIdx.x & 63;
     const int64_t tiles_n = (a.d_out + 32 * TN - 1) / (32 * TN);
@@ -451,72 +451,77 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    for (int kb = 0; kb < ks_used; kb += KB) {
-        const int nsteps = min(KB, ks_used - kb);
-        if constexpr (DT == DT_BF16) {
-            uint4 af[KB][TM], bh[KB][TN], bl[KB][TN];
+    // software pipeline over contraction steps with two register sets used
+    // in turn: the fragments of step s+1 are in flight while step s runs its
+    // MFMAs (past the last step the last one is re-read, never used)
+    const int last = ks_used - 1;
+    if constexpr (DT == DT_BF16) {
+        uint4 a0[TM], h0[TN], l0[TN], a1[TM], h1[TN], l1[TN];
+        auto fetch = [&](int ks, uint4* fa, uint4* fh, uint4* fl) {
+            const int64_t o = (int64_t)ks * 64;
 #pragma unroll
-            for (int st = 0; st < KB; ++st) {
-                if (st < nsteps) {
-                    const int64_t o = (int64_t)(kb + st) * 64;
+            for (int i = 0; i < TM; ++i) fa[i] = ab[i][o];
 #pragma unroll
-                    for (int i = 0; i < TM; ++i) af[st][i] = ab[i][o];
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        bh[st][j] = bb[j][o];
-                        bl[st][j] = bb[j][o + lo_off];
-                    }
-                }
+            for (int j = 0; j < TN; ++j) {
+                fh[j] = bb[j][o];
+                fl[j] = bb[j][o + lo_off];
             }
+            pin_issued_loads();
+        };
+        auto step = [&](const uint4* fa, const uint4* fh, const uint4* fl) {
 #pragma unroll
-            for (int st = 0; st < KB; ++st) {
-                if (st < nsteps) {
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j) {
-                            const bf16x8 x = __builtin_bit_cast(bf16x8, af[st][i]);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                x, __builtin_bit_cast(bf16x8, bh[st][j]), acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                x, __builtin_bit_cast(bf16x8, bl[st][j]), acc[i][j], 0, 0, 0);
-                        }
+                for (int j = 0; j < TN; ++j) {
+                    const bf16x8 x = __builtin_bit_cast(bf16x8, fa[i]);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, fh[j]),
+                                                                        acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, fl[j]),
+                                                                        acc[i][j], 0, 0, 0);
                 }
-            }
-        } else {
-            // piece h of lane group g holds chunks 16ks + 8h + 4g + 0..3;
-            // MFMA (h, e) takes element e: chunks 16ks + 8h + e and + 4
-            float4 af[KB][TM][2], bf[KB][TN][2];
+        };
+        if (ks_used > 0) fetch(0, a0, h0, l0);
+        for (int ks = 0; ks < ks_used; ks += 2) {
+            fetch(min(ks + 1, last), a1, h1, l1);
+            step(a0, h0, l0);
+            fetch(min(ks + 2, last), a0, h0, l0);
+            if (ks + 1 < ks_used) step(a1, h1, l1);
+        }
+    } else {
+        // piece h of lane group g holds chunks 16ks + 8h + 4g + 0..3;
+        // MFMA (h, e) takes element e: chunks 16ks + 8h + e and + 4
+        float4 a0[TM][2], b0[TN][2], a1[TM][2], b1[TN][2];
+        auto fetch = [&](int ks, float4 (*fa)[2], float4 (*fb)[2]) {
 #pragma unroll
-            for (int st = 0; st < KB; ++st) {
-                if (st < nsteps) {
+            for (int h = 0; h < 2; ++h) {
+                const int64_t o = ((int64_t)ks * 2 + h) * 64;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[i][h] = __builtin_bit_cast(float4, ab[i][o]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fb[j][h] = __builtin_bit_cast(float4, bb[j][o]);
+            }
+            pin_issued_loads();
+        };
+        auto step = [&](const float4 (*fa)[2], const float4 (*fb)[2]) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int64_t o = ((int64_t)(kb + st) * 2 + h) * 64;
-#pragma unroll
-                        for (int i = 0; i < TM; ++i) af[st][i][h] = __builtin_bit_cast(float4, ab[i][o]);
-#pragma unroll
-                        for (int j = 0; j < TN; ++j) bf[st][j][h] = __builtin_bit_cast(float4, bb[j][o]);
+                        const float4 x = fa[i][h], y = fb[j][h];
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc[i][j], 0, 0, 0);
                     }
-                }
-            }
-#pragma unroll
-            for (int st = 0; st < KB; ++st) {
-                if (st < nsteps) {
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const float4 x = af[st][i][h], y = bf[st][j][h];
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc[i][j], 0, 0, 0);
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc[i][j], 0, 0, 0);
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc[i][j], 0, 0, 0);
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc[i][j], 0, 0, 0);
-                            }
-                }
-            }
+        };
+        if (ks_used > 0) fetch(0, a0, b0);
+        for (int ks = 0; ks < ks_used; ks += 2) {
+            fetch(min(ks + 1, last), a1, b1);
+            step(a0, b0);
+            fetch(min(ks + 2, last), a0, b0);
+            if (ks + 1 < ks_used) step(a1, b1);
         }
     }
 
