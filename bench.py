@@ -13,7 +13,10 @@ Generator sets for all steps are drawn on the host beforehand and uploaded.
 Prints one JSON line: tokens/s for the whole job, per-call times, a roofline
 entry for the dominant kernel (HIP events around its launches on the stream
 it runs on) and the CPU oracle timed on a bounded sample of the same
-workload (cpu_baseline).
+workload (cpu_baseline).  An event record costs the GPU a few microseconds,
+so events bracket the calls of every --sample-every'th timed step only, and
+each such step also records an empty event pair whose interval (the cost of
+the event packets themselves) is subtracted from the per-call intervals.
 """
 from __future__ import annotations
 
@@ -41,6 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama7b_qkv")
+    p.add_argument("--sample-every", type=int, default=10,
+                   help="record per-call HIP events on every this many'th timed step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle's timed sample")
     p.add_argument("--cpu-cols", type=int, default=6144, help="dW columns of the oracle's timed sample")
@@ -168,6 +173,7 @@ def main():
         pamm.wgrad(C, f, a, dYb[i % 2], dW=dW, workspace=wws)
         if ev is not None:
             ev[2].record(stream)
+            ev[3].record(stream)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -175,18 +181,23 @@ def main():
     torch.cuda.synchronize()
     kept = float((f >= 0).float().mean().item())
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # sampled steps sit mid-window: the first timed step follows a host sync,
+    # and its events would also time the host catching up with the GPU
+    every = max(1, args.sample_every)
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for i in range(every // 2, args.steps, every)} or {0: [torch.cuda.Event(enable_timing=True) for _ in range(4)]}
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs.get(i))
     t_submit = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
-    t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps  # ms
-    t_wgrad = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_event = sum(e[2].elapsed_time(e[3]) for e in evs.values()) / len(evs)  # ms, empty pair
+    t_comp = sum(e[0].elapsed_time(e[1]) for e in evs.values()) / len(evs) - t_event
+    t_wgrad = sum(e[1].elapsed_time(e[2]) for e in evs.values()) / len(evs) - t_event
     kept = float((f >= 0).float().mean().item())
 
     cb, cf, rb, pb, pf = algorithmic(p, kept)
@@ -227,6 +238,8 @@ def main():
             "kept_fraction": round(kept, 4),
             "host_sampling_us": round(t_sample * 1e6, 2),
             "host_submit_us_per_step": round(t_submit * 1e6 / args.steps, 2),
+            "event_sampled_steps": len(evs),
+            "event_pair_us_subtracted": round(t_event * 1e3, 2),
         },
     }
     if not args.no_cpu_baseline:

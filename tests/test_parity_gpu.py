@@ -93,6 +93,18 @@ def test_long_segments_split_into_chunks():
     full_case(X, dY, g, 0.0, "long-segments")
 
 
+@pytest.mark.parametrize("n,d,dout,k", [
+    (65536, 32, 64, 1024),   # 64 sort blocks, 1024 generators
+    (65537, 32, 64, 40),     # a last sort block of one row
+    (6000, 64, 96, 4096),    # the largest k (LDS beyond 64 KB in the sort)
+])
+def test_sort_block_edges_and_largest_k(n, d, dout, k):
+    X = synth.clustered_activations(n, d, 64, seed=n + k, dtype="bf16")
+    dY = synth.gradients(n, dout, seed=n + dout, dtype="bf16")
+    g = pamm.sample_generators(n, k, seed=k + 3).numpy()
+    full_case(X, dY, g, 0.05, "sort-path")
+
+
 # --------------------------------------------------------------------------
 # degenerate cases the method has
 # --------------------------------------------------------------------------
