@@ -402,7 +402,10 @@ static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStrea
 }
 
 // Tile shapes per generator-tile width: rows per wave, waves, generators,
-// register prefetch depth (stages), bytes of each row per stage.
+// register prefetch depth (stages), bytes of each row per stage.  The
+// 256-generator tile prefetches two stages: with four, its accumulators,
+// fragments and ring exceed the 256 registers a wave of a 512-thread
+// workgroup may hold, and the spills cost twice the time.
 #ifndef PAMM_COMPRESS_RS16
 #define PAMM_COMPRESS_RS16 16, 8, 16, 4, 128
 #endif
@@ -416,7 +419,7 @@ static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStrea
 #define PAMM_COMPRESS_RS128 16, 8, 128, 4, 128
 #endif
 #ifndef PAMM_COMPRESS_RS256
-#define PAMM_COMPRESS_RS256 16, 8, 256, 4, 128
+#define PAMM_COMPRESS_RS256 16, 8, 256, 2, 128
 #endif
 
 template <int DT>

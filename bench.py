@@ -33,8 +33,9 @@ if ROOT not in sys.path:
 METRIC = "PAMM compress+wgrad tokens/sec; MFMA % peak and HBM GB/s % peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-# factor turning the FETCH_SIZE/WRITE_SIZE counters into bytes, from a plain
-# copy of known size; filled from profiles/ when the counters were taken
+# HBM bytes per compress launch on the llama-7B QKV workload, from the
+# FETCH_SIZE/WRITE_SIZE counters scaled by what they read for a plain copy of
+# known size; used while the kernel sources still match the ones profiled
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_llama7b_qkv_traffic.json")
 
 
@@ -205,7 +206,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": "compress_kernel (pamm_compress)", "achieved": round(comp_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None, "algorithmic_bytes_per_launch": cb, "avg_launch_us": round(t_comp * 1e3, 2)}
-    if os.path.exists(TRAFFIC_FILE):
+    if name == "llama7b_qkv" and os.path.exists(TRAFFIC_FILE):
         try:
             tr = json.load(open(TRAFFIC_FILE))
             if tr.get("kernel_source_hash") == source_hash():
