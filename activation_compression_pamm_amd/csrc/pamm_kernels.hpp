@@ -15,6 +15,9 @@ constexpr int kMaxTileGens = 256;
 constexpr int kChunkRows = 256;
 // Rows handled by one block of the wgrad counting sort.
 constexpr int kSortBlockRows = 1024;
+// Above this many histogram entries (sort blocks x generators) the histogram
+// is prefixed once instead of being summed by every sort block.
+constexpr int64_t kSortPrefixEntries = 8192;
 
 struct PartialBest {
     float score;  // best |<x,c>|/|c| in the tile, -1 if none
@@ -44,7 +47,7 @@ hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st);
 struct WgradLayout {
     int64_t nb;         // sort blocks
     int64_t max_chunks; // upper bound on row chunks
-    size_t off_hist, off_seg, off_nchunks, off_chunk_gen, off_chunk_begin, off_chunk_count;
+    size_t off_hist, off_tot, off_nchunks, off_chunk_gen, off_chunk_begin, off_chunk_count;
     size_t off_perm, off_palpha, off_AT, off_BT;
     int64_t ks_cap;     // 16-chunk contraction steps the product operands hold
     size_t total;

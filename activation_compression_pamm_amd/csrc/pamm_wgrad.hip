@@ -124,6 +124,43 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
     for (int j = threadIdx.x; j < k; j += 256) hist[(int64_t)blockIdx.x * k + j] = cnt[j];
 }
 
+// 1'. when the histogram is large (many blocks x many generators): turn it,
+// in place, into per-block exclusive prefixes along the blocks, and write the
+// segment sizes, so that each sort block reads 2k numbers instead of nb*k.
+// 64 generators per workgroup, the blocks split into 4 ranges, one per wave.
+__global__ __launch_bounds__(256) void sort_prefix_kernel(int32_t* __restrict__ hist, int64_t nb, int k,
+                                                          int32_t* __restrict__ totals) {
+    constexpr int B = 16;  // histogram rows loaded together
+    __shared__ int s_sum[4][64];
+    const int c = threadIdx.x & 63, seg = threadIdx.x >> 6;
+    const int j = blockIdx.x * 64 + c;
+    const int64_t len = (nb + 3) / 4, r0 = min(nb, seg * len), r1 = min(nb, r0 + len);
+    const int jj = min(j, k - 1);  // lanes past k read a valid column, write nothing
+    int sum = 0;
+    for (int64_t b0 = r0; b0 < r1; b0 += B) {
+        int h[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) h[u] = b0 + u < r1 ? hist[(b0 + u) * k + jj] : 0;
+#pragma unroll
+        for (int u = 0; u < B; ++u) sum += h[u];
+    }
+    s_sum[seg][c] = sum;
+    __syncthreads();
+    int run = 0;
+    for (int w = 0; w < seg; ++w) run += s_sum[w][c];
+    if (seg == 3 && j < k) totals[j] = run + sum;
+    for (int64_t b0 = r0; b0 < r1; b0 += B) {
+        int h[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) h[u] = b0 + u < r1 ? hist[(b0 + u) * k + jj] : 0;
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            if (b0 + u < r1 && j < k) hist[(b0 + u) * k + j] = run;
+            run += h[u];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 2. stable counting-sort scatter (+ segment offsets and chunk list)
 // ---------------------------------------------------------------------------
@@ -134,8 +171,8 @@ struct SortScatterArgs {
     int k;
     int nbits;
     int64_t nb;
-    const int32_t* hist;
-    int32_t* seg_start;    // [k + 1]
+    const int32_t* hist;   // [nb][k] per-block counts, or (PREFIXED) exclusive prefixes along the blocks
+    const int32_t* totals; // [k] segment sizes (PREFIXED only)
     int32_t* nchunks;      // [1]
     int32_t* chunk_gen;    // [max_chunks]
     int32_t* chunk_begin;  // [max_chunks]
@@ -144,6 +181,7 @@ struct SortScatterArgs {
     float* palpha;         // [n]
 };
 
+template <bool PREFIXED>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     extern __shared__ int s_dyn[];
     const int k = a.k;
@@ -167,12 +205,19 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     }
 
     // segment sizes and the rows of each generator that precede this block:
-    // the whole histogram is read with coalesced, independent loads and
-    // summed with LDS integer atomics (exact, so the order does not matter)
-    for (int j = t; j < k; j += 256) { s_tot[j] = 0; s_base[j] = 0; }
+    // read from the prefixed histogram, or, for a small histogram, summed
+    // here from all of it with coalesced, independent loads and LDS integer
+    // atomics (exact, so the order does not matter)
     for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
-    __syncthreads();
-    {
+    if constexpr (PREFIXED) {
+        for (int j = t; j < k; j += 256) {
+            s_tot[j] = a.totals[j];
+            s_base[j] = a.hist[b * k + j];
+        }
+        __syncthreads();
+    } else {
+        for (int j = t; j < k; j += 256) { s_tot[j] = 0; s_base[j] = 0; }
+        __syncthreads();
         const int64_t total = a.nb * k;
         const int64_t pre_end = b * k;  // entries of blocks before this one
 #pragma unroll 8
@@ -184,8 +229,8 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
                 if (e < pre_end) atomicAdd(&s_base[j], h);
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // block 0 cuts every generator's rows into chunks (before s_tot becomes starts)
     if (b == 0) {
@@ -199,8 +244,6 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
 
     const int total_rows = block_exclusive_scan(s_tot, k, s_tmp);  // s_tot := segment starts
     if (b == 0) {
-        for (int j = t; j < k; j += 256) a.seg_start[j] = s_tot[j];
-        if (t == 0) a.seg_start[k] = total_rows;
         const int* s_nch = s_w;
         for (int j = t; j < k; j += 256) {
             const int start = s_tot[j];
@@ -327,30 +370,47 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
     const int nch = *a.nchunks;
     const int ks_used = (nch + 15) >> 4;
     const int64_t a_slots = (a.d + 31) / 32 * ks_used * (DT == DT_BF16 ? 1 : 2);
-    const int64_t nitems = a_slots + (int64_t)ks_used * 16 * a.nslab;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-    for (int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); item < nitems;
-         item += wstride) {
-        if (item < a_slots) {
-            write_a_slot<DT>(a, item, ks_used, nch, lane);
-            continue;
+    for (int64_t slot = wave; slot < a_slots; slot += wstride) write_a_slot<DT>(a, slot, ks_used, nch, lane);
+
+    // one batch is the 64 rows the wave's row groups take together
+    static_assert(RG * U == 64, "a batch is 64 rows");
+    const int64_t nitems = (int64_t)ks_used * 16 * a.nslab;
+    auto meta = [&](int64_t it, int& bg, int& cn) {
+        const int64_t c = it / a.nslab;
+        bg = c < nch ? a.chunk_begin[c] : 0;
+        cn = c < nch ? a.chunk_count[c] : 0;
+    };
+    auto ids = [&](int bg, int cn, int t0, int* ii, float* aa) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tt = t0 + RG * u;
+            ii[u] = tt < cn ? a.perm[bg + tt] : -1;
+            aa[u] = tt < cn ? a.palpha[bg + tt] : 0.f;
         }
-        const int64_t ch = (item - a_slots) / a.nslab;
-        const int64_t col = ((item - a_slots) % a.nslab) * SC + lq * PE;
-        const int begin = ch < nch ? a.chunk_begin[ch] : 0;
-        const int cnt = ch < nch ? a.chunk_count[ch] : 0;
+    };
+    // the chunk list entry and the first batch's row ids of the wave's next
+    // item are fetched while the current item streams its dY rows
+    int begin = 0, cnt = 0;
+    int ii[U];
+    float aa[U];
+    if (wave < nitems) {
+        meta(wave, begin, cnt);
+        ids(begin, cnt, g, ii, aa);
+    }
+    for (int64_t item = wave; item < nitems; item += wstride) {
+        const int64_t next = item + wstride;
+        int nbegin = 0, ncnt = 0;
+        if (next < nitems) meta(next, nbegin, ncnt);
+        const int64_t ch = item / a.nslab;
+        const int64_t col = (item % a.nslab) * SC + lq * PE;
         float acc[PE];
 #pragma unroll
         for (int e = 0; e < PE; ++e) acc[e] = 0.f;
-        for (int t0 = g; t0 < cnt; t0 += RG * U) {
-            int ii[U];
-            float aa[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tt = t0 + RG * u;
-                ii[u] = tt < cnt ? a.perm[begin + tt] : -1;
-                aa[u] = tt < cnt ? a.palpha[begin + tt] : 0.f;
-            }
+        const int nbatch = (cnt + 63) >> 6;
+        for (int bt = 0; bt < nbatch; ++bt) {
+            if (bt > 0) ids(begin, cnt, g + 64 * bt, ii, aa);
             uint4 vv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -367,6 +427,9 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
                 for (int e = 0; e < PE; ++e) acc[e] = __builtin_fmaf(aa[u], v[e], acc[e]);
             }
         }
+        if (next < nitems) ids(nbegin, ncnt, g, ii, aa);
+        begin = nbegin;
+        cnt = ncnt;
         // fixed-order combine of the row groups
 #pragma unroll
         for (int m = LPR; m < 64; m <<= 1)
@@ -564,7 +627,7 @@ WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out) {
     L.max_chunks = (n + kChunkRows - 1) / kChunkRows + k;
     size_t off = 0;
     L.off_hist = off; off = align256(off + sizeof(int32_t) * (size_t)(L.nb * (k > 0 ? k : 1)));
-    L.off_seg = off; off = align256(off + sizeof(int32_t) * (size_t)(k + 1));
+    L.off_tot = off; off = align256(off + sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
     L.off_nchunks = off; off = align256(off + sizeof(int32_t));
     L.off_chunk_gen = off; off = align256(off + sizeof(int32_t) * (size_t)L.max_chunks);
     L.off_chunk_begin = off; off = align256(off + sizeof(int32_t) * (size_t)L.max_chunks);
@@ -585,7 +648,7 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     const WgradLayout& L = a.L;
     char* ws = a.ws;
     int32_t* hist = reinterpret_cast<int32_t*>(ws + L.off_hist);
-    int32_t* seg = reinterpret_cast<int32_t*>(ws + L.off_seg);
+    int32_t* tot = reinterpret_cast<int32_t*>(ws + L.off_tot);
     int32_t* nchunks = reinterpret_cast<int32_t*>(ws + L.off_nchunks);
     int32_t* cgen = reinterpret_cast<int32_t*>(ws + L.off_chunk_gen);
     int32_t* cbeg = reinterpret_cast<int32_t*>(ws + L.off_chunk_begin);
@@ -601,15 +664,23 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         int nbits = 0;
         while ((1 << nbits) < k) ++nbits;
         s.nbits = nbits;
-        s.nb = L.nb; s.hist = hist; s.seg_start = seg; s.nchunks = nchunks;
+        s.nb = L.nb; s.hist = hist; s.totals = tot; s.nchunks = nchunks;
         s.chunk_gen = cgen; s.chunk_begin = cbeg; s.chunk_count = ccnt; s.perm = perm; s.palpha = palpha;
         const size_t lds = sizeof(int) * (6 * (size_t)k + 256);
+        const bool prefixed = L.nb * k > kSortPrefixEntries;
+        const void* fn = prefixed ? reinterpret_cast<const void*>(&sort_scatter_kernel<true>)
+                                  : reinterpret_cast<const void*>(&sort_scatter_kernel<false>);
         if (lds > 65536) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sort_scatter_kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)L.nb), dim3(256), lds, st, s);
+        if (prefixed) {
+            hipLaunchKernelGGL(sort_prefix_kernel, dim3((unsigned)((k + 63) / 64)), dim3(256), 0, st, hist, L.nb, k,
+                               tot);
+            hipLaunchKernelGGL(sort_scatter_kernel<true>, dim3((unsigned)L.nb), dim3(256), lds, st, s);
+        } else {
+            hipLaunchKernelGGL(sort_scatter_kernel<false>, dim3((unsigned)L.nb), dim3(256), lds, st, s);
+        }
 
         ScatterArgs r;
         r.dY = reinterpret_cast<const char*>(a.dY);
