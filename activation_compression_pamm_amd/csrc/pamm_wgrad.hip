@@ -73,25 +73,30 @@ __device__ __forceinline__ uint64_t match_lanes(int v, bool valid, int nbits) {
 __device__ __forceinline__ void pin_issued_loads() { asm volatile("" ::: "memory"); }
 
 // Exclusive prefix sum over s[0..len) in LDS with a 256-thread block; returns
-// the total.  `tmp` needs 256 ints of LDS.
+// the total.  Each thread sums a run of `per` entries; the 256 run sums are
+// scanned with shuffles inside each wave and across the four wave totals.
+// `tmp` needs 4 ints of LDS.
 __device__ int block_exclusive_scan(int* s, int len, int* tmp) {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int per = (len + 255) / 256;
-    const int b = t * per, e = min(len, b + per);
+    const int b = min(len, t * per), e = min(len, b + per);
     int sum = 0;
     for (int j = b; j < e; ++j) sum += s[j];
-    tmp[t] = sum;
-    __syncthreads();
-    // Hillis-Steele over the 256 partial sums
-    for (int off = 1; off < 256; off <<= 1) {
-        const int v = t >= off ? tmp[t - off] : 0;
-        __syncthreads();
-        tmp[t] += v;
-        __syncthreads();
+    int inc = sum;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
     }
-    const int total = tmp[255];
-    int run = t > 0 ? tmp[t - 1] : 0;
+    if (lane == 63) tmp[wave] = inc;
     __syncthreads();
+    int run = inc - sum, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int x = tmp[w];
+        if (w < wave) run += x;
+        total += x;
+    }
     for (int j = b; j < e; ++j) {
         const int v = s[j];
         s[j] = run;
