@@ -107,7 +107,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int MT, int NTL>
 __device__ __forceinline__ void epilogue_rows(const CompressArgs& a, const f32x4 (&acc)[MT][NTL],
                                               const float (&xn2r)[MT], const float* s_cn2, const float* s_rinv,
-                                              int64_t row_base, int gen0, int ktile, int lane) {
+                                              int64_t row_base, int tile, int gen0, int ktile, int lane) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -146,8 +146,8 @@ __device__ __forceinline__ void epilogue_rows(const CompressArgs& a, const f32x4
                     pb.score = found ? bs : -1.0f;
                     pb.gen = found ? bg : -1;
                     pb.alpha = al;
-                    a.partial[(int64_t)blockIdx.y * a.n + row] = pb;
-                    if (blockIdx.y == 0) a.xn2[row] = xn2;
+                    a.partial[(int64_t)tile * a.n + row] = pb;
+                    if (tile == 0) a.xn2[row] = xn2;
                 } else {
                     // cosine of the winner; 0 for a zero row, NaN (never kept) for a NaN row
                     const float cs = xn2 == 0.f ? 0.f : bs / sqrtf(xn2);
@@ -189,8 +189,20 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int64_t m0 = (int64_t)blockIdx.x * BM;
-    const int gen0 = blockIdx.y * KN;
+    // workgroup -> (row block, generator tile).  With several tiles, the
+    // tiles of one row block take consecutive workgroup slots of one XCD
+    // (slots go round-robin over the 8 XCDs) and walk the stages in the same
+    // order, so the row block's X lines come from HBM about once and are
+    // re-read from that XCD's L2 by the other tiles.
+    int64_t rb = blockIdx.x;
+    int tile = 0;
+    if (a.ntiles > 1) {
+        const int64_t grp = blockIdx.x / (8 * a.ntiles), rem = blockIdx.x % (8 * a.ntiles);
+        tile = (int)(rem / 8);
+        rb = grp * 8 + rem % 8;
+    }
+    const int64_t m0 = rb * BM;
+    const int gen0 = tile * KN;
     const int ktile = min(KN, a.k - gen0);
     const int nst = (int)((a.d + E - 1) / E);
     const int last = nst - 1;
@@ -200,8 +212,8 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     if (a.C) {
         const int64_t row_chunks = (a.d + P - 1) / P;
         const int64_t total = (int64_t)a.k * row_chunks;
-        const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
-        const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        const int64_t nwg = gridDim.x;
+        const int64_t wg = blockIdx.x;
         for (int64_t c = wg * (64 * NW) + tid; c < total; c += nwg * (64 * NW)) {
             const int64_t j = c / row_chunks, col = (c % row_chunks) * P;
             int64_t r = a.gen_idx[j];
@@ -221,6 +233,8 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
             }
         }
     }
+
+    if (m0 >= a.n) return;  // slot past the last row block (whole workgroup)
 
     // ---- rows this lane fetches: load i covers tile rows RPI*(wave + NW*i) + lane/CH,
     // 16-byte chunk lane%CH of each RB-byte stage
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     }
     // rotated stage order (workgroups start at different column ranges);
     // padding stages past the end map to the last stage and are zeroed
-    const int rot = PAMM_COMPRESS_ROTATE ? (int)((blockIdx.x * 37u) % (unsigned)nst) : 0;
+    const int rot = PAMM_COMPRESS_ROTATE ? (int)(((uint64_t)rb * 37u) % (unsigned)nst) : 0;
     auto stage_of = [&](int s) { if (s >= nst) return last; int t = s + rot; return t >= nst ? t - nst : t; };
     const int tail_elems = (int)(a.d - (int64_t)last * E);
 
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
         xn2r[mt] = v;
     }
     __syncthreads();
-    epilogue_rows<MT, NTL>(a, acc, xn2r, s_cn2, s_rinv, m0 + wave * WM, gen0, ktile, lane);
+    epilogue_rows<MT, NTL>(a, acc, xn2r, s_cn2, s_rinv, m0 + wave * WM, tile, gen0, ktile, lane);
 }
 
 // Pick, per row, the best of the per-tile winners (tiles are in increasing
@@ -396,7 +410,8 @@ __global__ __launch_bounds__(256) void compress_empty_kernel(int64_t n, int32_t*
 template <int DT, int WM, int NW, int KN, int PD, int RB>
 static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStream_t st) {
     constexpr int BM = WM * NW;
-    dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)ntiles);
+    const int64_t nrb = (a.n + BM - 1) / BM;
+    const dim3 grid((unsigned)(ntiles > 1 ? (nrb + 7) / 8 * 8 * ntiles : nrb));
     hipLaunchKernelGGL((compress_rs_kernel<DT, WM, NW, KN, PD, RB>), grid, dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
@@ -443,6 +458,7 @@ hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st) {
     while (kn < a.k && kn < kMaxTileGens) kn *= 2;
     const int ntiles = (int)((a.k + kn - 1) / kn);
     CompressArgs b = a;
+    b.ntiles = ntiles;
     if (ntiles == 1) { b.partial = nullptr; b.xn2 = nullptr; }
     hipError_t e = dtype == DT_BF16 ? compress_dispatch<DT_BF16>(b, kn, ntiles, st)
                                     : compress_dispatch<DT_F32>(b, kn, ntiles, st);

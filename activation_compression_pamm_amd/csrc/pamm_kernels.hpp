@@ -39,6 +39,7 @@ struct CompressArgs {
     float* alpha;
     PartialBest* partial;  // [ntiles x n] when k > kMaxTileGens
     float* xn2;            // [n] when k > kMaxTileGens
+    int ntiles;            // generator tiles (set by the launcher)
 };
 
 hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st);
