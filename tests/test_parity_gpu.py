@@ -105,6 +105,29 @@ def test_sort_block_edges_and_largest_k(n, d, dout, k):
     full_case(X, dY, g, 0.05, "sort-path")
 
 
+def _random_case(i):
+    # shapes, generator counts and thresholds drawn from one seeded stream;
+    # row lengths a multiple of 16 bytes (the ABI's leading-dimension rule)
+    rng = np.random.default_rng(9000 + i)
+    dtype = "bf16" if i % 3 else "f32"
+    per = 8 if dtype == "bf16" else 4
+    n = int(rng.integers(1, 5000))
+    d = per * int(rng.integers(1, 512 // per + 1))
+    dout = per * int(rng.integers(1, 640 // per + 1))
+    k = int(rng.integers(1, min(n, 600) + 1))
+    eps = float(rng.choice([0.0, 0.05, 0.2, 0.5]))
+    return dtype, n, d, dout, k, eps
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes(i):
+    dtype, n, d, dout, k, eps = _random_case(i)
+    X = synth.clustered_activations(n, d, max(2, min(64, k)), seed=100 + i, dtype=dtype)
+    dY = synth.gradients(n, dout, seed=200 + i, dtype=dtype)
+    g = pamm.sample_generators(n, k, seed=300 + i).numpy()
+    full_case(X, dY, g, eps, f"random-{i}")
+
+
 # --------------------------------------------------------------------------
 # degenerate cases the method has
 # --------------------------------------------------------------------------
