@@ -115,16 +115,20 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ hist) {
     extern __shared__ int s_dyn[];
     int* cnt = s_dyn;
+    // all of this thread's rows are loaded first: their latency overlaps the
+    // clearing of the bins, and none is counted before all have arrived
+    const int64_t r0 = (int64_t)blockIdx.x * kSortBlockRows;
+    int fv[kSortBlockRows / 256];
+#pragma unroll
+    for (int u = 0; u < kSortBlockRows / 256; ++u) {
+        const int64_t i = r0 + u * 256 + threadIdx.x;
+        fv[u] = i < n ? f[i] : -1;
+    }
     for (int j = threadIdx.x; j < k; j += 256) cnt[j] = 0;
     __syncthreads();
-    const int64_t r0 = (int64_t)blockIdx.x * kSortBlockRows;
-    for (int r = threadIdx.x; r < kSortBlockRows; r += 256) {
-        const int64_t i = r0 + r;
-        if (i < n) {
-            const int fi = f[i];
-            if (fi >= 0 && fi < k) atomicAdd(&cnt[fi], 1);
-        }
-    }
+#pragma unroll
+    for (int u = 0; u < kSortBlockRows / 256; ++u)
+        if (fv[u] >= 0 && fv[u] < k) atomicAdd(&cnt[fv[u]], 1);
     __syncthreads();
     for (int j = threadIdx.x; j < k; j += 256) hist[(int64_t)blockIdx.x * k + j] = cnt[j];
 }
@@ -213,27 +217,39 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     // read from the prefixed histogram, or, for a small histogram, summed
     // here from all of it with coalesced, independent loads and LDS integer
     // atomics (exact, so the order does not matter)
-    for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
     if constexpr (PREFIXED) {
+        for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
         for (int j = t; j < k; j += 256) {
             s_tot[j] = a.totals[j];
             s_base[j] = a.hist[b * k + j];
         }
         __syncthreads();
     } else {
-        for (int j = t; j < k; j += 256) { s_tot[j] = 0; s_base[j] = 0; }
-        __syncthreads();
+        // the first HB histogram entries of this thread are loaded before
+        // the bins are cleared, so their latency overlaps the clearing
+        constexpr int HB = 8;
         const int64_t total = a.nb * k;
         const int64_t pre_end = b * k;  // entries of blocks before this one
-#pragma unroll 8
-        for (int64_t e = t; e < total; e += 256) {
-            const int h = a.hist[e];
+        int hv[HB];
+#pragma unroll
+        for (int u = 0; u < HB; ++u) {
+            const int64_t e = t + 256 * u;
+            hv[u] = e < total ? a.hist[e] : 0;
+        }
+        for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
+        for (int j = t; j < k; j += 256) { s_tot[j] = 0; s_base[j] = 0; }
+        __syncthreads();
+        auto add = [&](int64_t e, int h) {
             if (h) {
                 const int j = (int)(e % k);
                 atomicAdd(&s_tot[j], h);
                 if (e < pre_end) atomicAdd(&s_base[j], h);
             }
-        }
+        };
+#pragma unroll
+        for (int u = 0; u < HB; ++u) add(t + 256 * u, hv[u]);
+#pragma unroll 8
+        for (int64_t e = t + 256 * HB; e < total; e += 256) add(e, a.hist[e]);
         __syncthreads();
     }
 
