@@ -8,12 +8,16 @@
 //
 // Kernels, in stream order:
 //   1. sort_hist       per block of 1024 rows: count of rows per generator.
+//   1'. sort_prefix    only when the histogram is large (blocks x generators
+//                      above kSortPrefixEntries): turns it in place into
+//                      per-block prefixes along the blocks plus segment sizes.
 //   2. sort_scatter    stable counting sort of the kept rows by generator:
 //                      every block rebuilds the global segment offsets from
-//                      the histograms (a few KB, L2-resident), ranks its rows
-//                      with wave ballots and writes (row, alpha) in generator
-//                      order; block 0 also cuts each generator's rows into
-//                      chunks of at most kChunkRows rows.
+//                      the histograms (a few KB, L2-resident) or reads its
+//                      prefixes, ranks its rows with wave ballots and writes
+//                      (row, alpha) in generator order; block 0 also cuts
+//                      each generator's rows into chunks of at most
+//                      kChunkRows rows.
 //   3. scatter_reduce  gathers the product's A operand (each chunk's
 //                      generator row of C, in MFMA fragment order), then
 //                      one wave per (chunk, 128-byte column slab): sums
