@@ -28,7 +28,10 @@
 //     (lowest index on ties, NaN never wins), cosine test against eps, alpha =
 //     S_if / |c_f|^2.
 // When k exceeds one generator tile the per-tile winners go to a small
-// workspace and compress_merge_kernel picks the overall winner.
+// workspace and compress_merge_kernel picks the overall winner.  The tiles of
+// one row block then take consecutive workgroup slots of one XCD and walk the
+// stages in the same order, so the row block's X lines come from HBM about
+// once and are re-read from that XCD's L2.
 #include <type_traits>
 
 #include "pamm_device.hpp"

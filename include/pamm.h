@@ -24,6 +24,8 @@
  *     aligned and their leading dimensions multiples of 16 bytes (8 bf16 or
  *     4 fp32 elements); f, alpha and gen_idx need 4-byte alignment; the
  *     workspace needs 256-byte alignment.
+ *   - A workspace holds a call's intermediate results until its kernels
+ *     finish: calls that may run concurrently need workspaces of their own.
  *   - Every call returns a pamm_status_t.  Arguments are fully validated
  *     before anything is enqueued; on any error nothing is launched and no
  *     output is written.  No C++ exception crosses this interface.
@@ -127,7 +129,8 @@ size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out,
  *   ws       workspace of at least pamm_wgrad_workspace_size bytes
  *
  * Rows with f outside [0, k) (the -1 of dropped rows) are skipped and their
- * dY rows are never read.  Rows are grouped by generator with a stable
+ * dY rows are never read; with no kept row (or k = 0) dW is zero (unchanged
+ * when accumulating).  Rows are grouped by generator with a stable
  * counting sort and summed in a fixed order, so the result is bitwise
  * deterministic.  fp32 accumulation; for bf16 the generator product splits
  * B~ into two bf16 terms (about 16 significant bits), for fp32 it uses fp32
