@@ -250,12 +250,19 @@ def main():
 
 
 def source_hash() -> str:
+    """Hash of the kernel sources with comments and blank lines removed, so
+    that documentation edits keep the profiled traffic figure attached."""
     import hashlib
+    import re
     h = hashlib.sha256()
     src = os.path.join(ROOT, "activation_compression_pamm_amd", "csrc")
     for fn in sorted(os.listdir(src)):
         if fn.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(src, fn), "rb").read())
+            text = open(os.path.join(src, fn), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+            h.update(code.encode())
     return h.hexdigest()[:16]
 
 
