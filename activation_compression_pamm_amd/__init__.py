@@ -44,8 +44,8 @@ _EXPORTS = {
                                                     ctypes.c_int]),
     "pamm_wgrad": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
-                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
-                                  ctypes.c_void_p]),
+                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]),
     "pamm_decompress": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]),
@@ -114,6 +114,21 @@ def _rows(t, name):
     return t.shape[0], t.shape[1], t.stride(0)
 
 
+def _on_gpu(where, **tensors):
+    """Every tensor argument must live on one GPU: the kernels read and write
+    them in place."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{where}: {name} must be on the GPU, got device {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{where}: {name} is on {t.device}, expected {dev}")
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
@@ -157,6 +172,7 @@ def compress(X, gen_idx, eps: float, *, C=None, f=None, alpha=None, workspace=No
     gen_idx: int32 device tensor of k generator row ids (see sample_generators).
     Returns (C [k x d], f [n] int32, alpha [n] fp32)."""
     torch = _torch()
+    _on_gpu("compress", X=X, C=C, f=f, alpha=alpha, workspace=workspace)
     n, d, ldx = _rows(X, "X")
     dt = _dtype_code(X)
     gen_idx = gen_idx.to(device=X.device, dtype=torch.int32).contiguous()
@@ -175,22 +191,30 @@ def compress(X, gen_idx, eps: float, *, C=None, f=None, alpha=None, workspace=No
     return C, f, alpha
 
 
-def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, workspace=None, stream=None):
+def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: bool = False, workspace=None,
+          stream=None):
     """Approximate weight gradient dW = C^T B~ [d x d_out] (fp32) from the
-    compressed triple and the output gradient dY [n x d_out]."""
+    compressed triple and the output gradient dY [n x d_out].  With
+    transpose_out the result is dW^T [d_out x d], the layout of the weight
+    gradient of a layer Y = X W^T."""
     torch = _torch()
+    _on_gpu("wgrad", C=C, f=f, alpha=alpha, dY=dY, dW=dW, workspace=workspace)
     k, d = C.shape
     n, d_out, lddy = _rows(dY, "dY")
     dt = _dtype_code(dY)
     if C.dtype != dY.dtype:
         raise TypeError("C and dY must share a dtype")
+    shape = (d_out, d) if transpose_out else (d, d_out)
     if dW is None:
-        dW = torch.empty((d, d_out), dtype=torch.float32, device=dY.device)
+        dW = torch.empty(shape, dtype=torch.float32, device=dY.device)
+    if tuple(dW.shape) != shape or dW.dtype != torch.float32:
+        raise ValueError(f"dW must be float32 of shape {shape}, got {tuple(dW.shape)} {dW.dtype}")
     _, _, lddw = _rows(dW, "dW")
     ws = _workspace(wgrad_workspace_size(n, k, d, d_out, dt), dY.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = load_library().pamm_wgrad(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, _ptr(dY), d_out, lddy, dt, _ptr(dW), lddw,
-                                   1 if accumulate else 0, _ptr(ws), nbytes, _stream_ptr(stream))
+                                   1 if accumulate else 0, 1 if transpose_out else 0, _ptr(ws), nbytes,
+                                   _stream_ptr(stream))
     _check(st, "pamm_wgrad")
     return dW
 
@@ -198,11 +222,14 @@ def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, workspace=None,
 def decompress(C, f, alpha, *, out=None, stream=None):
     """Reconstruction X~_i = alpha_i C_f(i) (zero rows where f = -1)."""
     torch = _torch()
+    _on_gpu("decompress", C=C, f=f, alpha=alpha, out=out)
     k, d = C.shape
     n = f.numel()
     dt = _dtype_code(C)
     if out is None:
         out = torch.empty((n, d), dtype=C.dtype, device=f.device)
+    if tuple(out.shape) != (n, d) or out.dtype != C.dtype:
+        raise ValueError(f"out must be {C.dtype} of shape {(n, d)}, got {tuple(out.shape)} {out.dtype}")
     _, _, ldxt = _rows(out, "out")
     st = load_library().pamm_decompress(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, dt, _ptr(out), ldxt,
                                         _stream_ptr(stream))

@@ -140,11 +140,11 @@ size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out,
 }
 
 int pamm_wgrad(const void* C, const int32_t* f, const float* alpha, int64_t n, int64_t k, int64_t d, const void* dY,
-               int64_t d_out, int64_t lddy, int dtype, float* dW, int64_t lddw, int accumulate, void* ws,
-               size_t ws_bytes, void* stream) {
+               int64_t d_out, int64_t lddy, int dtype, float* dW, int64_t lddw, int accumulate, int transpose_out,
+               void* ws, size_t ws_bytes, void* stream) {
     if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
     if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || d_out < 1 ||
-        d_out > kMaxRows || (n > 0 && lddy < d_out) || lddw < d_out)
+        d_out > kMaxRows || (n > 0 && lddy < d_out) || lddw < (transpose_out ? d : d_out))
         return PAMM_ERR_SHAPE;
     if (!dW || (n > 0 && (!f || !alpha || !dY)) || (k > 0 && !C)) return PAMM_ERR_NULL;
     if (!aligned(dW, 16) || lddw % 4 != 0) return PAMM_ERR_ALIGN;
@@ -169,6 +169,7 @@ int pamm_wgrad(const void* C, const int32_t* f, const float* alpha, int64_t n, i
     a.dW = dW;
     a.lddw = lddw;
     a.accumulate = accumulate ? 1 : 0;
+    a.transpose_out = transpose_out ? 1 : 0;
     a.ws = reinterpret_cast<char*>(ws);
     a.L = L;
     a.num_cus = num_cus();

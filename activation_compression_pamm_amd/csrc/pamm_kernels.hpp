@@ -66,9 +66,10 @@ struct WgradArgs {
     const void* dY;
     int64_t d_out;
     int64_t lddy_bytes;
-    float* dW;
+    float* dW;              // [d x d_out], or [d_out x d] when transpose_out
     int64_t lddw;
     int accumulate;
+    int transpose_out;
     char* ws;
     WgradLayout L;
     int num_cus;

@@ -508,15 +508,23 @@ struct GemmArgs {
     int64_t lddw;
 };
 
-template <int DT, int TM, int TN, bool ACC>
+// TRANS writes dW^T [d_out x d] instead: the two operands swap places in
+// every MFMA (their fragments share one lane layout), so each 32x32 result
+// is a tile of dW^T and the stores are still whole 128-byte row pieces.
+template <int DT, int TM, int TN, bool ACC, bool TRANS>
 __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
     constexpr int PIECES = DT == DT_BF16 ? 1 : 2;
     const int lane = threadIdx.x & 63;
+    // consecutive waves take consecutive tiles along the output's rows, so
+    // a workgroup's stores extend the same rows: along d_out for dW, along d
+    // for dW^T
+    const int64_t tiles_m = (a.d + 32 * TM - 1) / (32 * TM);
     const int64_t tiles_n = (a.d_out + 32 * TN - 1) / (32 * TN);
     const int64_t wt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t tm = wt / tiles_n, tn = wt % tiles_n;
+    const int64_t tm = TRANS ? wt % tiles_m : wt / tiles_n;
+    const int64_t tn = TRANS ? wt / tiles_m : wt % tiles_n;
     const int64_t m0 = tm * 32 * TM, n0 = tn * 32 * TN;
-    if (m0 >= a.d) return;
+    if (m0 >= a.d || n0 >= a.d_out) return;
     const int ks_used = (*a.nchunks + 15) >> 4;
     const int64_t mblk = (a.d + 31) / 32, nblk = (a.d_out + 31) / 32;
     const uint4* AF = reinterpret_cast<const uint4*>(a.AF);
@@ -562,10 +570,14 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const bf16x8 x = __builtin_bit_cast(bf16x8, fa[i]);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, fh[j]),
-                                                                        acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, fl[j]),
-                                                                        acc[i][j], 0, 0, 0);
+                    const bf16x8 h = __builtin_bit_cast(bf16x8, fh[j]), l = __builtin_bit_cast(bf16x8, fl[j]);
+                    if constexpr (TRANS) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h, x, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l, x, acc[i][j], 0, 0, 0);
+                    } else {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, h, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, l, acc[i][j], 0, 0, 0);
+                    }
                 }
         };
         if (ks_used > 0) fetch(0, a0, h0, l0);
@@ -597,7 +609,7 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const float4 x = fa[i][h], y = fb[j][h];
+                        const float4 x = TRANS ? fb[j][h] : fa[i][h], y = TRANS ? fa[i][h] : fb[j][h];
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc[i][j], 0, 0, 0);
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc[i][j], 0, 0, 0);
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc[i][j], 0, 0, 0);
@@ -613,19 +625,23 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
         }
     }
 
-    // element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32 of a 32x32 tile
+    // element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32 of a
+    // 32x32 tile: rows in d and columns in d_out, or the other way round
+    // for TRANS (rows in d_out, columns in d)
     const bool interior = m0 + 32 * TM <= a.d && n0 + 32 * TN <= a.d_out;
+    const int64_t nrows = TRANS ? a.d_out : a.d, ncols = TRANS ? a.d : a.d_out;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + 32 * j + (lane & 31);
-            float* base = a.dW + (m0 + 32 * i + 4 * (lane >> 5)) * a.lddw + col;
+            const int64_t row0 = TRANS ? n0 + 32 * j : m0 + 32 * i;
+            const int64_t col = (TRANS ? m0 + 32 * i : n0 + 32 * j) + (lane & 31);
+            float* base = a.dW + (row0 + 4 * (lane >> 5)) * a.lddw + col;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = 8 * (e >> 2) + (e & 3);
                 float* p = base + r * a.lddw;
-                if (interior || (m0 + 32 * i + 4 * (lane >> 5) + r < a.d && col < a.d_out)) {
+                if (interior || (row0 + 4 * (lane >> 5) + r < nrows && col < ncols)) {
                     // non-temporal: dW goes straight to HBM instead of parking
                     // ~200 MB of dirty lines in the memory-side cache, whose
                     // write-back would otherwise slow the next kernel
@@ -733,10 +749,20 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     const int64_t waves = ((a.d + 32 * PAMM_GEMM_TM - 1) / (32 * PAMM_GEMM_TM)) *
                           ((a.d_out + 32 * PAMM_GEMM_TN - 1) / (32 * PAMM_GEMM_TN));
     const dim3 grid((unsigned)((waves + 3) / 4));
-    if (a.accumulate)
-        hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, true>), grid, dim3(256), 0, st, g);
-    else
-        hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, false>), grid, dim3(256), 0, st, g);
+    if (a.transpose_out) {
+        if (a.accumulate)
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, true, true>), grid, dim3(256), 0, st, g);
+        else
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, false, true>), grid, dim3(256), 0, st,
+                               g);
+    } else {
+        if (a.accumulate)
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, true, false>), grid, dim3(256), 0, st,
+                               g);
+        else
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, false, false>), grid, dim3(256), 0, st,
+                               g);
+    }
     return hipGetLastError();
 }
 

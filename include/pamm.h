@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PAMM_ABI_VERSION 1
+#define PAMM_ABI_VERSION 2
 /* Largest generator count the segment sort of pamm_wgrad supports. */
 #define PAMM_MAX_K 4096
 
@@ -124,8 +124,11 @@ size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out,
  *   C        [k x d] dtype, f [n] int32, alpha [n] fp32  (read; the triple
  *            saved by pamm_compress)
  *   dY       [n x d_out], leading dimension lddy, dtype  (read)
- *   dW       [d x d_out] fp32, leading dimension lddw    (written; when
- *            `accumulate` is non-zero the result is added to dW)
+ *   dW       [d x d_out] fp32, leading dimension lddw >= d_out (written;
+ *            when `accumulate` is non-zero the result is added to dW); with
+ *            `transpose_out` non-zero it is dW^T [d_out x d], lddw >= d, the
+ *            orientation of a framework's weight gradient for a layer
+ *            Y = X W^T (same values, written directly in that layout)
  *   ws       workspace of at least pamm_wgrad_workspace_size bytes
  *
  * Rows with f outside [0, k) (the -1 of dropped rows) are skipped and their
@@ -139,7 +142,7 @@ size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out,
 int pamm_wgrad(const void *C, const int32_t *f, const float *alpha,
                int64_t n, int64_t k, int64_t d,
                const void *dY, int64_t d_out, int64_t lddy, int dtype,
-               float *dW, int64_t lddw, int accumulate,
+               float *dW, int64_t lddw, int accumulate, int transpose_out,
                void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pamm_abi_version() == 1
+    assert lib.pamm_abi_version() == 2
     for s in range(9):
         assert lib.pamm_status_string(s)
     assert lib.pamm_status_string(12345) == b"unknown status"
@@ -106,10 +106,10 @@ def test_compress_validation(lib):
 
 
 def call_wgrad(lib, C=FAKE, f=FAKE, a=FAKE, n=64, k=4, d=32, dY=FAKE, dout=48, lddy=48, dt=1, dW=FAKE, lddw=48,
-               acc=0, ws=FAKE, wsb=None):
+               acc=0, tr=0, ws=FAKE, wsb=None):
     if wsb is None:
         wsb = lib.pamm_wgrad_workspace_size(n, k, d, dout, dt)
-    return lib.pamm_wgrad(C, f, a, n, k, d, dY, dout, lddy, dt, dW, lddw, acc, ws, wsb, None)
+    return lib.pamm_wgrad(C, f, a, n, k, d, dY, dout, lddy, dt, dW, lddw, acc, tr, ws, wsb, None)
 
 
 def test_wgrad_validation(lib):
@@ -127,6 +127,10 @@ def test_wgrad_validation(lib):
     assert call_wgrad(lib, ws=None) == EWS
     assert call_wgrad(lib, wsb=1024) == EWS
     assert call_wgrad(lib, ws=FAKE + 64) == EALIGN
+    # transposed output: dW^T [d_out x d] needs lddw >= d
+    assert call_wgrad(lib, tr=1, d=64, lddw=48) == ESHAPE
+    assert call_wgrad(lib, tr=1, d=32, lddw=30) == ESHAPE
+    assert call_wgrad(lib, tr=1, d=32, lddw=34) == EALIGN
 
 
 def test_decompress_validation(lib):
