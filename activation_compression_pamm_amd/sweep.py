@@ -1,0 +1,73 @@
+"""Error of PAMM's weight gradient against the exact X^T dY, over k and eps.
+
+"QKV Projections Require a Fraction of Their Memory", section 2, sub-part
+"Scelta dei Parametri": the ratio k/b can go down to 1/512, and dropping the
+proximity constraint works best.  This sweep measures, on the seeded
+synthetic workload of the 1B sweep (n = 32768, d = 2048, d_out = 6144,
+clustered activations, Gaussian gradients), the relative Frobenius error
+||dW_pamm - X^T dY|| / ||X^T dY|| and the kept fraction for every (k, eps).
+It reports; it asserts nothing: with gradients drawn independently of the
+activations the error mostly measures how much of X the generators span.
+
+    python -m activation_compression_pamm_amd.sweep [--ks 1024,256,128,64] [--eps 0,0.1,0.2,0.5]
+
+The exact product is a plain library GEMM in fp32 on the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+
+
+def run(ks, epss, workload="llama1b_sweep"):
+    import numpy as np
+    import torch
+
+    import activation_compression_pamm_amd as pamm
+    from activation_compression_pamm_amd import synth
+
+    X, dY, p = synth.make_config(workload)
+    n, d, d_out = p["n"], p["d"], p["d_out"]
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    Xd, dYd = dev(X), dev(dY)
+    exact = Xd.float().t().contiguous() @ dYd.float()  # [d x d_out] in fp32
+    norm = exact.norm().item()
+    rows = []
+    for k in ks:
+        g = pamm.sample_generators(n, k, synth.generator_seed(workload)).cuda()
+        for eps in epss:
+            C, f, a = pamm.compress(Xd, g, eps)
+            dW = pamm.wgrad(C, f, a, dYd)
+            err = (dW - exact).norm().item() / norm
+            kept = (f >= 0).float().mean().item()
+            rows.append({"k": k, "n_over_k": n // k, "eps": eps, "kept_fraction": round(kept, 4),
+                         "rel_error": round(err, 4)})
+    torch.cuda.synchronize()
+    return {"workload": workload, "n": n, "d": d, "d_out": d_out, "rows": rows}
+
+
+def to_markdown(res) -> str:
+    lines = [f"Workload {res['workload']}: n = {res['n']}, d = {res['d']}, d_out = {res['d_out']}", "",
+             "| k | n/k | eps | kept fraction | rel. error of dW vs X^T dY |", "|---|---|---|---|---|"]
+    for r in res["rows"]:
+        lines.append(f"| {r['k']} | {r['n_over_k']} | {r['eps']} | {r['kept_fraction']:.4f} | {r['rel_error']:.4f} |")
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--ks", default="1024,256,128,64")
+    ap.add_argument("--eps", default="0,0.1,0.2,0.5")
+    ap.add_argument("--json", action="store_true", help="print JSON instead of a markdown table")
+    args = ap.parse_args()
+    res = run([int(x) for x in args.ks.split(",")], [float(x) for x in args.eps.split(",")])
+    print(json.dumps(res) if args.json else to_markdown(res))
+
+
+if __name__ == "__main__":
+    main()

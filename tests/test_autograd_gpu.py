@@ -98,3 +98,14 @@ def test_pamm_linear_with_every_row_a_generator_is_exact():
     torch.cuda.synchronize()
     exact = dY.double().cpu().T @ X.detach().double().cpu()
     assert rel(layer.weight.grad.double().cpu().numpy(), exact.numpy()) <= TOL["f32"]
+
+
+def test_error_sweep_runs_and_reports_sane_values():
+    from activation_compression_pamm_amd import sweep
+    say("sweep", "llama1b_sweep k=64 eps=0,0.1")
+    res = sweep.run([64], [0.0, 0.1])
+    r0, r1 = res["rows"]
+    assert r0["kept_fraction"] == 1.0                  # eps = 0 keeps every row
+    assert 0.0 < r1["kept_fraction"] < 1.0
+    assert 0.0 < r0["rel_error"] < 1.0 and 0.0 < r1["rel_error"] < 1.0
+    assert "| 64 | 512 | 0.0 |" in sweep.to_markdown(res)
