@@ -123,6 +123,7 @@ int pamm_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int dtype, c
     a.c_vec_ok = (d * elem_size(dtype)) % 16 == 0;
     a.f = f;
     a.alpha = alpha;
+    a.num_cus = num_cus();
     if (need > 0) {
         const int64_t ntiles = (k + pamm::kMaxTileGens - 1) / pamm::kMaxTileGens;
         const size_t part = sizeof(pamm::PartialBest) * (size_t)(ntiles * n);

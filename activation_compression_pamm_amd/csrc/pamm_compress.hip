@@ -100,6 +100,38 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// C = X[gen_idx]: every workgroup of the launch copies its share of the
+// generator rows (the launch's workgroups together cover all k rows).
+template <int DT>
+__device__ __forceinline__ void copy_out_generators(const CompressArgs& a, int nthreads) {
+    if (!a.C) return;
+    const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
+    constexpr int P = Elem<DT>::per16;
+    const int tid = threadIdx.x;
+    const int64_t row_chunks = (a.d + P - 1) / P;
+    const int64_t total = (int64_t)a.k * row_chunks;
+    const int64_t nwg = gridDim.x;
+    const int64_t wg = blockIdx.x;
+    for (int64_t c = wg * nthreads + tid; c < total; c += nwg * nthreads) {
+        const int64_t j = c / row_chunks, col = (c % row_chunks) * P;
+        int64_t r = a.gen_idx[j];
+        r = r < 0 ? 0 : (r >= a.n ? a.n - 1 : r);
+        const uint4 v = load16_tail<DT>(X + r * a.ldx_bytes, col, a.d);
+        char* dst = reinterpret_cast<char*>(a.C) + (j * a.d + col) * Elem<DT>::size;
+        if (a.c_vec_ok && col + P <= a.d) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < P && col + e < a.d; ++e) {
+                if constexpr (DT == DT_BF16)
+                    reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                else
+                    reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // Per-row winner among a generator tile, then the eps test and alpha.
@@ -211,31 +243,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     const int last = nst - 1;
     const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
 
-    // ---- copy out the generator rows C = X[gen_idx] (spread over all workgroups)
-    if (a.C) {
-        const int64_t row_chunks = (a.d + P - 1) / P;
-        const int64_t total = (int64_t)a.k * row_chunks;
-        const int64_t nwg = gridDim.x;
-        const int64_t wg = blockIdx.x;
-        for (int64_t c = wg * (64 * NW) + tid; c < total; c += nwg * (64 * NW)) {
-            const int64_t j = c / row_chunks, col = (c % row_chunks) * P;
-            int64_t r = a.gen_idx[j];
-            r = r < 0 ? 0 : (r >= a.n ? a.n - 1 : r);
-            const uint4 v = load16_tail<DT>(X + r * a.ldx_bytes, col, a.d);
-            char* dst = reinterpret_cast<char*>(a.C) + (j * a.d + col) * Elem<DT>::size;
-            if (a.c_vec_ok && col + P <= a.d) {
-                *reinterpret_cast<uint4*>(dst) = v;
-            } else {
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                for (int e = 0; e < P && col + e < a.d; ++e) {
-                    if constexpr (DT == DT_BF16)
-                        reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                    else
-                        reinterpret_cast<uint32_t*>(dst)[e] = w[e];
-                }
-            }
-        }
-    }
+    copy_out_generators<DT>(a, 64 * NW);
 
     if (m0 >= a.n) return;  // slot past the last row block (whole workgroup)
 
@@ -381,6 +389,335 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     epilogue_rows<MT, NTL>(a, acc, xn2r, s_cn2, s_rinv, m0 + wave * WM, tile, gen0, ktile, lane);
 }
 
+// Tiles of 256 generators in bf16: the contraction dominates (k >= 256 means
+// at least 256 MFMA flops per byte of X), so the workgroup is shaped like a
+// GEMM tile: NWR x NWC waves, each holding 32*MT rows x 32*NT generators of
+// S in 32x32 MFMA accumulators (256 registers at 4 x 4: the whole
+// accumulation register file), so one LDS fragment read feeds 4 MFMAs.
+//   * One stage = 64 elements (128 bytes) of every tile row.  X and C lines
+//     are fetched as whole 128-byte lines into registers one stage ahead and
+//     written to a double-buffered, XOR-swizzled LDS tile (as above).  The
+//     steady-state loop has no branch: the stage count is padded to an even
+//     number, and padding stages and the columns past d are masked to zero
+//     on their way into LDS.
+//   * |x_i|^2 and |c_j|^2 are summed in fp32 with bf16 dot2 instructions
+//     from the staged lines, each element once per workgroup.  (The smaller-tile kernels take |c_j|^2 from the
+//     MFMA instead, which makes alpha exact for a power-of-two multiple of a
+//     generator; here no accumulation registers are left for that, so such an
+//     alpha is exact to a few fp32 ulps, and its bf16 reconstruction is still
+//     exact.)
+//   * Epilogue, through the then free stage ring: each wave writes its block
+//     of S row by row and two lanes per row scan it; the NWC column winners
+//     meet in LDS, and one thread per row merges them (lower column first,
+//     so the lowest index wins ties) and writes the result.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float sumsq_dot2(const v4u32& v, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // copy the component out first: this compiler bit-casts a vector
+        // component expression as if it were component 0
+        const uint32_t e = v[w];
+        const bf16x2 h = __builtin_bit_cast(bf16x2, e);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(h, h, acc, false);
+    }
+    return acc;
+}
+
+template <int MT, int NT, int NWR, int NWC>
+__global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressArgs a) {
+    constexpr int RB = 128;                 // bytes of a row per stage
+    constexpr int E = RB / 2;               // elements per stage
+    constexpr int NW = NWR * NWC;
+    constexpr int NTH = 64 * NW;
+    constexpr int WM = 32 * MT, WN = 32 * NT;
+    constexpr int BM = WM * NWR, BN = WN * NWC;
+    constexpr int XPT = BM * 8 / NTH;       // 16-byte X chunks per lane per stage
+    constexpr int CPT = BN * 8 / NTH;
+    static_assert(BN == kMaxTileGens, "one generator tile per workgroup");
+    static_assert((BM * 8) % NTH == 0 && (BN * 8) % NTH == 0, "tile shape");
+
+    // two stage buffers, each the X tile then the C tile
+    constexpr int TILE = (BM + BN) * RB;
+    __shared__ __align__(16) char s_tile[2 * TILE];
+    __shared__ __align__(16) float s_cn2[BN];
+    __shared__ __align__(16) float s_rinv[BN];
+    __shared__ float s_ms[NWC][BM];
+    __shared__ int s_mg[NWC][BM];
+    __shared__ float s_md[NWC][BM];
+    __shared__ float s_xn2[BM];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wr = wave / NWC, wc = wave % NWC;
+    // workgroup -> (row block, generator tile), as in compress_rs_kernel
+    int64_t rb = blockIdx.x;
+    int tile = 0;
+    if (a.ntiles > 1) {
+        const int64_t grp = blockIdx.x / (8 * a.ntiles), rem = blockIdx.x % (8 * a.ntiles);
+        tile = (int)(rem / 8);
+        rb = grp * 8 + rem % 8;
+    }
+    const int64_t m0 = rb * BM;
+    const int gen0 = tile * BN;
+    const int ktile = min(BN, a.k - gen0);
+    const int nst = (int)((a.d + E - 1) / E);
+    const int npos = (nst + 1) & ~1;        // stage positions, padded to even
+    const int last = nst - 1;
+    const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
+
+    copy_out_generators<DT_BF16>(a, NTH);
+
+    if (m0 >= a.n) return;  // slot past the last row block (whole workgroup)
+
+    // load i of a lane covers tile row (NTH/8)*i + tid/8 (8 lanes per row, one
+    // 128-byte line per row and wave-wide load), 16-byte chunk tid%8.  Loads
+    // address a wave-uniform base plus a 32-bit per-lane row offset (the
+    // launcher only picks this kernel when X spans less than 4 GiB).
+    const int qc = tid & 7;
+    const int rsub = tid >> 3;
+    uint32_t xoff[XPT], coff[CPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        int64_t g = m0 + (NTH / 8) * i + rsub;
+        if (g >= a.n) g = a.n - 1;  // padding rows: any valid row, results unused
+        xoff[i] = (uint32_t)((g - m0) * a.ldx_bytes);
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int jj = min((NTH / 8) * i + rsub, ktile - 1);  // padding generators: any valid one, masked later
+        int64_t g = a.gen_idx[gen0 + jj];
+        g = g < 0 ? 0 : (g >= a.n ? a.n - 1 : g);
+        coff[i] = (uint32_t)(g * a.ldx_bytes);
+    }
+    // LDS slot of load i: row (NTH/8)*i + rsub, chunk qc, swizzled by row%8
+    // (the same for every i, so slot i is slot 0 plus a constant)
+    const int dst0 = swz<RB>(rsub, qc);
+    // stage at position p: workgroups start at different column ranges (as
+    // above); positions past the last stage re-read it and are zeroed
+    const int rot = PAMM_COMPRESS_ROTATE ? (int)(((uint64_t)rb * 37u) % (unsigned)nst) : 0;
+    auto stage_of = [&](int p) { if (p >= nst) return last; int t = p + rot; return t >= nst ? t - nst : t; };
+    const int tail_elems = (int)(a.d - (int64_t)last * E);
+    auto valid_elems = [&](int p) { return p >= nst ? 0 : (stage_of(p) == last ? tail_elems : E); };
+    const int64_t row_chunks = (a.row_bytes + 15) / 16;
+
+    v4u32 xr[XPT], cr[CPT];
+    // per-lane partial |x|^2 and |c|^2 of the rows this lane fetches
+    float xsq[XPT], csq[CPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xsq[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) csq[i] = 0.f;
+    auto issue = [&](int p) __attribute__((always_inline)) {
+        const int st = stage_of(p);
+        const char* bx = X + m0 * a.ldx_bytes + (int64_t)st * RB;
+        const char* bc = X + (int64_t)st * RB;
+        // chunks past the row end (tail stage) re-read the row's last chunk
+        const uint32_t q16 = (uint32_t)min((int64_t)qc, row_chunks - 1 - (int64_t)st * (RB / 16)) * 16u;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) xr[i] = *reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16));
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) cr[i] = *reinterpret_cast<const v4u32*>(bc + (coff[i] + q16));
+    };
+    // registers of position p -> an LDS buffer.  Elements at or past the
+    // position's valid count (the tail stage's columns past d, all of a
+    // padding position) are cleared with per-lane masks: no branch.
+    auto stash = [&](int p, char* buf) __attribute__((always_inline)) {
+        const int lim = valid_elems(p) - qc * 8;  // valid elements of this lane's chunk
+        v4u32 m;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            m[w] = (2 * w < lim ? 0x0000ffffu : 0u) | (2 * w + 1 < lim ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const v4u32 v = xr[i] & m;
+            *reinterpret_cast<v4u32*>(buf + dst0 + i * (NTH / 8) * RB) = v;
+            xsq[i] = sumsq_dot2(v, xsq[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const v4u32 v = cr[i] & m;
+            *reinterpret_cast<v4u32*>(buf + BM * RB + dst0 + i * (NTH / 8) * RB) = v;
+            csq[i] = sumsq_dot2(v, csq[i]);
+        }
+    };
+
+    f32x16 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x16{};
+
+    // fragment of 32x32x16: lane l holds row l%32 of the 32-row tile and
+    // elements 8*(l/32) .. +7 of the 16-element K step.  Every tile row the
+    // lane reads has row%8 = l%8, so a fragment's LDS address is one base per
+    // K step (the chunk swizzle) plus compile-time offsets.
+    const int frow = lane & 31, fk = lane >> 5;
+    int fa[E / 16];
+#pragma unroll
+    for (int ks = 0; ks < E / 16; ++ks) fa[ks] = frow * RB + ((((2 * ks + fk) ^ (frow & 7))) << 4);
+    const int xw = wr * WM * RB, cw = BM * RB + wc * WN * RB;
+    auto load_frags = [&](const char* buf, int ks, v4u32 (&xf)[MT], v4u32 (&cf)[NT]) __attribute__((always_inline)) {
+        const char* bx = buf + xw + fa[ks];
+        const char* bc = buf + cw + fa[ks];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xf[mt] = *reinterpret_cast<const v4u32*>(bx + mt * 32 * RB);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) cf[nt] = *reinterpret_cast<const v4u32*>(bc + nt * 32 * RB);
+    };
+    auto mfma_step = [&](const v4u32 (&xf)[MT], const v4u32 (&cf)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, xf[mt]), __builtin_bit_cast(bf16x8, cf[nt]), acc[mt][nt], 0, 0, 0);
+
+    };
+    // one stage: four K steps of 16; the fragments of step ks+1 are read
+    // from LDS while the MFMAs of step ks run (two register sets)
+    auto compute = [&](const char* buf) __attribute__((always_inline)) {
+        v4u32 xa[MT], ca[NT], xb[MT], cb[NT];
+        load_frags(buf, 0, xa, ca);
+#pragma unroll
+        for (int ks = 0; ks < E / 16; ks += 2) {
+            load_frags(buf, ks + 1, xb, cb);
+            mfma_step(xa, ca);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 2 < E / 16) load_frags(buf, ks + 2, xa, ca);
+            mfma_step(xb, cb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // compute position p from one buffer; stash position p+1 (fetched one
+    // step earlier) into the other; fetch position p+2
+    auto step = [&](int p, const char* cur, char* nxt) __attribute__((always_inline)) {
+        compute(cur);
+        stash(p + 1, nxt);
+        issue(min(p + 2, npos - 1));
+        wait_lds();
+        ring_barrier();
+    };
+
+    issue(0);
+    stash(0, s_tile);
+    issue(1);
+    wait_lds();
+    ring_barrier();
+    int p = 0;
+    for (; p + 2 < npos; p += 2) {
+        step(p, s_tile, s_tile + TILE);
+        step(p + 1, s_tile + TILE, s_tile);
+    }
+    step(p, s_tile, s_tile + TILE);
+    compute(s_tile + TILE);
+
+    // ---- epilogue (the stage ring is free now: every wave has passed the
+    // last compute, so waves reuse it as scratch after one more barrier)
+    __syncthreads();
+    float* ring = reinterpret_cast<float*>(s_tile);
+    // norms: each lane's partial sums of its 8 rows (X and C) go to LDS,
+    // one thread per tile row adds the 8 chunks
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) ring[((NTH / 8) * i + rsub) * 8 + qc] = xsq[i];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) ring[BM * 8 + ((NTH / 8) * i + rsub) * 8 + qc] = csq[i];
+    __syncthreads();
+    for (int r = tid; r < BM; r += NTH) {
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v += ring[r * 8 + q];
+        s_xn2[r] = v;
+    }
+    for (int r = tid; r < BN; r += NTH) {
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v += ring[BM * 8 + r * 8 + q];
+        s_cn2[r] = v;
+        s_rinv[r] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
+    }
+    __syncthreads();
+    // winners: in passes of 32 rows, each wave writes its 32 x WN block of
+    // S row-major (rows padded by 4 floats against bank conflicts); two lanes
+    // per row then scan WN/2 generators each in increasing order (lowest
+    // index on ties, NaN never wins) and the pair is merged.  Element i of a
+    // 32x32 result lane l is row 8*(i/4) + 4*(l/32) + i%4, generator l%32.
+    constexpr int PST = WN + 4;  // floats per staged row
+    float* wbuf = ring + wave * 32 * PST;
+    const int sr = lane >> 1, sh = lane & 1;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wbuf[(8 * (i >> 2) + 4 * fk + (i & 3)) * PST + nt * 32 + frow] = acc[mt][nt][i];
+        float bs = -1.0f, bd = 0.f;
+        int bg = 0x7fffffff;
+        const float* rowp = wbuf + sr * PST + sh * (WN / 2);
+#pragma unroll
+        for (int j = 0; j < WN / 2; j += 4) {
+            const f32x4 dv = *reinterpret_cast<const f32x4*>(rowp + j);
+            const int j0 = wc * WN + sh * (WN / 2) + j;
+            const f32x4 cv = *reinterpret_cast<const f32x4*>(s_cn2 + j0);
+            const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (j0 + e < ktile) {
+                    const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : 0.f;
+                    if (sc > bs) { bs = sc; bg = gen0 + j0 + e; bd = dv[e]; }
+                }
+            }
+        }
+        const float os = shfl_xor(bs, 1);
+        const int og = shfl_xor(bg, 1);
+        const float od = shfl_xor(bd, 1);
+        if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = od; }
+        if (sh == 0) {
+            const int rloc = wr * WM + mt * 32 + sr;
+            s_ms[wc][rloc] = bs;
+            s_mg[wc][rloc] = bg;
+            s_md[wc][rloc] = bd;
+        }
+    }
+    __syncthreads();
+    // ---- one thread per row: merge the column winners, eps test, write
+    for (int r = tid; r < BM; r += NTH) {
+        const int64_t row = m0 + r;
+        if (row >= a.n) continue;
+        float bs = s_ms[0][r], bd = s_md[0][r];
+        int bg = s_mg[0][r];
+#pragma unroll
+        for (int c = 1; c < NWC; ++c) {
+            const float os = s_ms[c][r];
+            const int og = s_mg[c][r];
+            if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = s_md[c][r]; }
+        }
+        const bool found = bg != 0x7fffffff;
+        float al = 0.f;
+        if (found) {
+            const float cn = s_cn2[bg - gen0];
+            al = cn > 0.f ? bd / cn : 0.f;
+        }
+        const float xn2 = s_xn2[r];
+        if (a.partial) {
+            PartialBest pb;
+            pb.score = found ? bs : -1.0f;
+            pb.gen = found ? bg : -1;
+            pb.alpha = al;
+            a.partial[(int64_t)tile * a.n + row] = pb;
+            if (tile == 0) a.xn2[row] = xn2;
+        } else {
+            const float cs = xn2 == 0.f ? 0.f : bs / sqrtf(xn2);
+            const bool keep = found && cs >= a.eps;
+            a.f[row] = keep ? bg : -1;
+            a.alpha[row] = keep ? al : 0.f;
+        }
+    }
+}
+
 // Pick, per row, the best of the per-tile winners (tiles are in increasing
 // generator order, so a strict comparison keeps the lowest index on ties) and
 // apply the eps test.
@@ -419,6 +756,15 @@ static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStrea
     return hipGetLastError();
 }
 
+template <int MT, int NT, int NWR, int NWC>
+static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStream_t st) {
+    constexpr int BM = 16 * MT * NWR;
+    const int64_t nrb = (a.n + BM - 1) / BM;
+    const dim3 grid((unsigned)(ntiles > 1 ? (nrb + 7) / 8 * 8 * ntiles : nrb));
+    hipLaunchKernelGGL((compress_gemm_kernel<MT, NT, NWR, NWC>), grid, dim3(64 * NWR * NWC), 0, st, a);
+    return hipGetLastError();
+}
+
 // Tile shapes per generator-tile width: rows per wave, waves, generators,
 // register prefetch depth (stages), bytes of each row per stage.  The
 // 256-generator tile prefetches two stages: with four, its accumulators,
@@ -439,6 +785,28 @@ static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStrea
 #ifndef PAMM_COMPRESS_RS256
 #define PAMM_COMPRESS_RS256 16, 8, 256, 2, 128
 #endif
+// bf16 tiles of 256 generators: rows and generators per wave (in 32s), waves
+// along rows and along generators.
+#ifndef PAMM_COMPRESS_GEMM
+#define PAMM_COMPRESS_GEMM 4, 4, 2, 2
+#endif
+#ifndef PAMM_COMPRESS_USE_GEMM
+#define PAMM_COMPRESS_USE_GEMM 1
+#endif
+
+// The GEMM-shaped kernel addresses X with 32-bit offsets from a uniform
+// base: every row offset, plus one stage, must stay below 4 GiB.  With one
+// workgroup per compute unit it also needs at least as many (row block,
+// generator tile) pairs as compute units; with fewer, the 128-row kernel,
+// which runs twice as many workgroups, finishes first.
+template <int MT, int NWR>
+static bool gemm_pays(const CompressArgs& a, int ntiles) {
+    constexpr int BM = 32 * MT * NWR;
+    const int64_t nrb = (a.n + BM - 1) / BM;
+    return (uint64_t)a.n * (uint64_t)a.ldx_bytes + 256u <= 0xffffffffull && nrb * ntiles >= a.num_cus;
+}
+template <int MT, int NT, int NWR, int NWC>
+static bool gemm_pays_cfg(const CompressArgs& a, int ntiles) { return gemm_pays<MT, NWR>(a, ntiles); }
 
 template <int DT>
 static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, hipStream_t st) {
@@ -447,7 +815,11 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
         case 32: return launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
         case 64: return launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
         case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
-        default: return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);
+        default:
+            if constexpr (DT == DT_BF16)
+                if (PAMM_COMPRESS_USE_GEMM && gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles))
+                    return launch_compress_gemm<PAMM_COMPRESS_GEMM>(a, ntiles, st);
+            return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);
     }
 }
 

@@ -40,6 +40,7 @@ struct CompressArgs {
     PartialBest* partial;  // [ntiles x n] when k > kMaxTileGens
     float* xn2;            // [n] when k > kMaxTileGens
     int ntiles;            // generator tiles (set by the launcher)
+    int num_cus;           // compute units of the device
 };
 
 hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st);

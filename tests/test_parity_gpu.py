@@ -149,6 +149,37 @@ def test_k_equals_n_gives_exact_product(dtype):
     assert e <= (1e-4 if dtype == "bf16" else 1e-5), e
 
 
+# bf16 with 256-generator tiles and at least one (row block, tile) pair per
+# compute unit: the GEMM-shaped compress kernel.  Ragged rows, a tail stage,
+# a padding stage position, a partial last tile and a strided view.
+GEMM_CASES = [
+    (65573, 136, 136, 256, 0.05),   # ragged n; tail stage of 8; odd stage count
+    (33000, 200, 200, 300, 0.1),    # two tiles, the last one 44 generators
+    (65536, 64, 64, 256, 0.0),      # a single stage (and one padding position)
+    (32768, 256, 256, 512, 0.0),    # two full tiles
+    (65536, 120, 144, 256, 0.1),    # strided view: ldx > d
+]
+
+
+@pytest.mark.parametrize("n,d,ldx,k,eps", GEMM_CASES)
+def test_gemm_tiles(n, d, ldx, k, eps):
+    Xbig = synth.clustered_activations(n, ldx, 64, seed=61 + d, dtype="bf16")
+    X = np.ascontiguousarray(Xbig[:, :d])
+    g = pamm.sample_generators(n, k, 62).numpy()
+    say("gemm-tiles", f"n={n} d={d} ldx={ldx} k={k} eps={eps}")
+    C, f, a = pamm.compress(to_dev(Xbig)[:, :d], torch.from_numpy(g).cuda(), eps)
+    torch.cuda.synchronize()
+    C_g, f_g, a_g = to_host(C), to_host(f), to_host(a)
+    stats = check_compress(X, g, eps, C_g, f_g, a_g)
+    # a generator's own row: itself (unless a duplicate row ties lower), alpha
+    # 1 to a few ulps (|c|^2 from fp32 dot2 sums, the dot from the MFMA)
+    own = f_g[g]
+    mine = own == np.arange(k)
+    assert np.all(own <= np.arange(k)) and np.mean(mine) > 0.99
+    assert np.all(np.abs(a_g[g][mine] - 1.0) <= 1e-5), np.abs(a_g[g][mine] - 1.0).max()
+    say("gemm-tiles", "ok", stats)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_scaled_copies_and_self_rows_exact(dtype):
     n, d = 700, 96
