@@ -32,6 +32,7 @@
 // one row block then take consecutive workgroup slots of one XCD and walk the
 // stages in the same order, so the row block's X lines come from HBM about
 // once and are re-read from that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "pamm_device.hpp"
@@ -400,12 +401,13 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
 //     steady-state loop has no branch: the stage count is padded to an even
 //     number, and padding stages and the columns past d are masked to zero
 //     on their way into LDS.
-//   * |x_i|^2 and |c_j|^2 are summed in fp32 with bf16 dot2 instructions
-//     from the staged lines, each element once per workgroup.  (The smaller-tile kernels take |c_j|^2 from the
-//     MFMA instead, which makes alpha exact for a power-of-two multiple of a
-//     generator; here no accumulation registers are left for that, so such an
-//     alpha is exact to a few fp32 ulps, and its bf16 reconstruction is still
-//     exact.)
+//   * |x_i|^2 is summed in fp32 with bf16 dot2 instructions from the staged
+//     lines by the workgroups of the first generator tile; |c_j|^2 likewise,
+//     once per generator, by gen_prep_kernel, which also writes C.  (The
+//     smaller-tile kernels take |c_j|^2 from the MFMA instead, which makes
+//     alpha exact for a power-of-two multiple of a generator; here no
+//     accumulation registers are left for that, so such an alpha is exact to
+//     a few fp32 ulps, and its bf16 reconstruction is still exact.)
 //   * Epilogue, through the then free stage ring: each wave writes its block
 //     of S row by row and two lanes per row scan it; the NWC column winners
 //     meet in LDS, and one thread per row merges them (lower column first,
@@ -468,8 +470,6 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     const int last = nst - 1;
     const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
 
-    copy_out_generators<DT_BF16>(a, NTH);
-
     if (m0 >= a.n) return;  // slot past the last row block (whole workgroup)
 
     // load i of a lane covers tile row (NTH/8)*i + tid/8 (8 lanes per row, one
@@ -503,45 +503,64 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     auto valid_elems = [&](int p) { return p >= nst ? 0 : (stage_of(p) == last ? tail_elems : E); };
     const int64_t row_chunks = (a.row_bytes + 15) / 16;
 
+    static_assert(XPT == 8 && CPT == 8, "the stash is split in four parts of four chunks");
     v4u32 xr[XPT], cr[CPT];
-    // per-lane partial |x|^2 and |c|^2 of the rows this lane fetches
-    float xsq[XPT], csq[CPT];
+    // per-lane partial |x|^2 of the rows this lane fetches (summed by the
+    // workgroups of the first generator tile only; |c|^2 comes from the
+    // generator pass, gen_prep_kernel)
+    float xsq[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) xsq[i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) csq[i] = 0.f;
-    auto issue = [&](int p) __attribute__((always_inline)) {
+    // fetch part `part` (four of the lane's 16 chunks: X for parts 0-1, C
+    // for parts 2-3) of position p into registers
+    auto issue_part = [&](int p, int part) __attribute__((always_inline)) {
         const int st = stage_of(p);
-        const char* bx = X + m0 * a.ldx_bytes + (int64_t)st * RB;
-        const char* bc = X + (int64_t)st * RB;
         // chunks past the row end (tail stage) re-read the row's last chunk
         const uint32_t q16 = (uint32_t)min((int64_t)qc, row_chunks - 1 - (int64_t)st * (RB / 16)) * 16u;
+        if (part < 2) {
+            const char* bx = X + m0 * a.ldx_bytes + (int64_t)st * RB;
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) xr[i] = *reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16));
+            for (int i = 4 * part; i < 4 * part + 4; ++i) xr[i] = *reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16));
+        } else {
+            const char* bc = X + (int64_t)st * RB;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) cr[i] = *reinterpret_cast<const v4u32*>(bc + (coff[i] + q16));
+            for (int i = 4 * (part - 2); i < 4 * (part - 2) + 4; ++i)
+                cr[i] = *reinterpret_cast<const v4u32*>(bc + (coff[i] + q16));
+        }
+    };
+    auto issue = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) issue_part(p, part);
     };
     // registers of position p -> an LDS buffer.  Elements at or past the
     // position's valid count (the tail stage's columns past d, all of a
     // padding position) are cleared with per-lane masks: no branch.
-    auto stash = [&](int p, char* buf) __attribute__((always_inline)) {
+    auto stage_mask = [&](int p) __attribute__((always_inline)) {
         const int lim = valid_elems(p) - qc * 8;  // valid elements of this lane's chunk
         v4u32 m;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
             m[w] = (2 * w < lim ? 0x0000ffffu : 0u) | (2 * w + 1 < lim ? 0xffff0000u : 0u);
+        return m;
+    };
+    auto stash_part = [&](const v4u32& m, char* buf, int part, auto wx) __attribute__((always_inline)) {
+        if (part < 2) {
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const v4u32 v = xr[i] & m;
-            *reinterpret_cast<v4u32*>(buf + dst0 + i * (NTH / 8) * RB) = v;
-            xsq[i] = sumsq_dot2(v, xsq[i]);
-        }
+            for (int i = 4 * part; i < 4 * part + 4; ++i) {
+                const v4u32 v = xr[i] & m;
+                *reinterpret_cast<v4u32*>(buf + dst0 + i * (NTH / 8) * RB) = v;
+                if constexpr (decltype(wx)::value) xsq[i] = sumsq_dot2(v, xsq[i]);
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const v4u32 v = cr[i] & m;
-            *reinterpret_cast<v4u32*>(buf + BM * RB + dst0 + i * (NTH / 8) * RB) = v;
-            csq[i] = sumsq_dot2(v, csq[i]);
+            for (int i = 4 * (part - 2); i < 4 * (part - 2) + 4; ++i)
+                *reinterpret_cast<v4u32*>(buf + BM * RB + dst0 + i * (NTH / 8) * RB) = cr[i] & m;
         }
+    };
+    auto stash = [&](int p, char* buf, auto wx) __attribute__((always_inline)) {
+        const v4u32 m = stage_mask(p);
+#pragma unroll
+        for (int part = 0; part < 4; ++part) stash_part(m, buf, part, wx);
     };
 
     f32x16 acc[MT][NT];
@@ -576,54 +595,89 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
                     __builtin_bit_cast(bf16x8, xf[mt]), __builtin_bit_cast(bf16x8, cf[nt]), acc[mt][nt], 0, 0, 0);
 
     };
-    // one stage: four K steps of 16; the fragments of step ks+1 are read
-    // from LDS while the MFMAs of step ks run (two register sets)
-    auto compute = [&](const char* buf) __attribute__((always_inline)) {
-        v4u32 xa[MT], ca[NT], xb[MT], cb[NT];
-        load_frags(buf, 0, xa, ca);
-#pragma unroll
-        for (int ks = 0; ks < E / 16; ks += 2) {
-            load_frags(buf, ks + 1, xb, cb);
-            mfma_step(xa, ca);
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks + 2 < E / 16) load_frags(buf, ks + 2, xa, ca);
-            mfma_step(xb, cb);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // compute position p from one buffer; stash position p+1 (fetched one
-    // step earlier) into the other; fetch position p+2
-    auto step = [&](int p, const char* cur, char* nxt) __attribute__((always_inline)) {
-        compute(cur);
-        stash(p + 1, nxt);
-        issue(min(p + 2, npos - 1));
+    // One stage position: four K steps of 16 with two fragment register sets
+    // in turn.  The schedule is skewed across the barrier: the fragments of
+    // step 0 of position p+1 are read after the barrier while the MFMAs of
+    // step 3 of position p run, so the barrier does not leave the matrix
+    // cores waiting on LDS.  The stash of position p+1 and the fetch of
+    // position p+2 are spread over the first three K steps' scheduling
+    // regions, next to MFMAs of position p.
+    // sched_barrier(0) fences keep the compiler from moving work across.
+    v4u32 xa[MT], ca[NT], xb[MT], cb[NT];
+    auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto body = [&](int p, const char* cur, char* nxt, auto wx) __attribute__((always_inline)) {
+        const v4u32 m = stage_mask(p + 1);
+        const int pf = min(p + 2, npos - 1);
+        load_frags(cur, 1, xb, cb);
+        mfma_step(xa, ca);                     // step 0 (read before the last barrier)
+        stash_part(m, nxt, 0, wx);
+        issue_part(pf, 0);
+        fence();
+        load_frags(cur, 2, xa, ca);
+        mfma_step(xb, cb);                     // step 1
+        stash_part(m, nxt, 1, wx);
+        issue_part(pf, 1);
+        fence();
+        load_frags(cur, 3, xb, cb);
+        mfma_step(xa, ca);                     // step 2
+        stash_part(m, nxt, 2, wx);
+        issue_part(pf, 2);
+        stash_part(m, nxt, 3, wx);
+        issue_part(pf, 3);
+        fence();
         wait_lds();
         ring_barrier();
+        fence();
+        load_frags(nxt, 0, xa, ca);            // step 0 of position p+1
+        mfma_step(xb, cb);                     // step 3
+        fence();
     };
+    auto tail = [&](const char* cur) __attribute__((always_inline)) {
+        load_frags(cur, 1, xb, cb);
+        mfma_step(xa, ca);
+        fence();
+        load_frags(cur, 2, xa, ca);
+        mfma_step(xb, cb);
+        fence();
+        load_frags(cur, 3, xb, cb);
+        mfma_step(xa, ca);
+        fence();
+        mfma_step(xb, cb);
+    };
+    static_assert(E / 16 == 4, "the skewed schedule is written for four K steps per stage");
 
-    issue(0);
-    stash(0, s_tile);
-    issue(1);
-    wait_lds();
-    ring_barrier();
-    int p = 0;
-    for (; p + 2 < npos; p += 2) {
-        step(p, s_tile, s_tile + TILE);
-        step(p + 1, s_tile + TILE, s_tile);
-    }
-    step(p, s_tile, s_tile + TILE);
-    compute(s_tile + TILE);
+    // the main loop, in two versions: with |x|^2 (first generator tile) or
+    // without (the other tiles; their |x|^2 would be the same)
+    auto run = [&](auto wx) __attribute__((always_inline)) {
+        issue(0);
+        stash(0, s_tile, wx);
+        issue(1);
+        wait_lds();
+        ring_barrier();
+        fence();
+        load_frags(s_tile, 0, xa, ca);
+        int p = 0;
+        for (; p + 2 < npos; p += 2) {
+            body(p, s_tile, s_tile + TILE, wx);
+            body(p + 1, s_tile + TILE, s_tile, wx);
+        }
+        body(p, s_tile, s_tile + TILE, wx);
+        tail(s_tile + TILE);
+    };
+    if (tile == 0)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
     // ---- epilogue (the stage ring is free now: every wave has passed the
     // last compute, so waves reuse it as scratch after one more barrier)
     __syncthreads();
     float* ring = reinterpret_cast<float*>(s_tile);
-    // norms: each lane's partial sums of its 8 rows (X and C) go to LDS,
-    // one thread per tile row adds the 8 chunks
+    // norms: each lane's partial |x|^2 of its 8 rows go to LDS, one thread
+    // per tile row adds the 8 chunks (zeros outside the first tile, where
+    // they are not used); |c|^2 from the generator pass
 #pragma unroll
     for (int i = 0; i < XPT; ++i) ring[((NTH / 8) * i + rsub) * 8 + qc] = xsq[i];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) ring[BM * 8 + ((NTH / 8) * i + rsub) * 8 + qc] = csq[i];
     __syncthreads();
     for (int r = tid; r < BM; r += NTH) {
         float v = 0.f;
@@ -632,9 +686,8 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         s_xn2[r] = v;
     }
     for (int r = tid; r < BN; r += NTH) {
-        float v = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v += ring[BM * 8 + r * 8 + q];
+        // a padding generator of a partial tile is marked by |c|^2 = -1
+        const float v = r < ktile ? a.cn2[gen0 + r] : -1.0f;
         s_cn2[r] = v;
         s_rinv[r] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
     }
@@ -665,16 +718,22 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if (j0 + e < ktile) {
-                    const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : 0.f;
-                    if (sc > bs) { bs = sc; bg = gen0 + j0 + e; bd = dv[e]; }
-                }
+                // selects, no branches: a padding generator (|c|^2 = -1)
+                // scores -1 and never wins; |c|^2 = 0 or NaN scores 0
+                const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : (cv[e] < 0.f ? -1.0f : 0.f);
+                const bool win = sc > bs;
+                bs = win ? sc : bs;
+                bg = win ? gen0 + j0 + e : bg;
+                bd = win ? dv[e] : bd;
             }
         }
         const float os = shfl_xor(bs, 1);
         const int og = shfl_xor(bg, 1);
         const float od = shfl_xor(bd, 1);
-        if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = od; }
+        const bool take = os > bs || (os == bs && og < bg);
+        bs = take ? os : bs;
+        bg = take ? og : bg;
+        bd = take ? od : bd;
         if (sh == 0) {
             const int rloc = wr * WM + mt * 32 + sr;
             s_ms[wc][rloc] = bs;
@@ -715,6 +774,35 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             a.f[row] = keep ? bg : -1;
             a.alpha[row] = keep ? al : 0.f;
         }
+    }
+}
+
+// Generator pass of the GEMM-shaped path: C = X[gen_idx] and |c_j|^2 (fp32
+// dot2 sums of the stored bf16 values), one wave per generator row.
+__global__ __launch_bounds__(256) void gen_prep_kernel(CompressArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
+    const int64_t row_chunks = (a.d + 7) / 8;
+    for (int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); j < a.k; j += nw) {
+        int64_t r = a.gen_idx[j];
+        r = r < 0 ? 0 : (r >= a.n ? a.n - 1 : r);
+        const char* src = X + r * a.ldx_bytes;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.C) + j * a.d;
+        float s = 0.f;
+        for (int64_t c = lane; c < row_chunks; c += 64) {
+            const uint4 u = load16_tail<DT_BF16>(src, c * 8, a.d);  // zeros past d
+            const v4u32 v = {u.x, u.y, u.z, u.w};
+            s = sumsq_dot2(v, s);
+            if (a.c_vec_ok && c * 8 + 8 <= a.d) {
+                *reinterpret_cast<uint4*>(dst + c * 8) = u;
+            } else {
+                for (int e = 0; e < 8 && c * 8 + e < a.d; ++e) dst[c * 8 + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) s += shfl_xor(s, m);
+        if (lane == 0) a.cn2[j] = s;
     }
 }
 
@@ -816,9 +904,15 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
         case 64: return launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
         case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
         default:
-            if constexpr (DT == DT_BF16)
-                if (PAMM_COMPRESS_USE_GEMM && gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles))
+            if constexpr (DT == DT_BF16) {
+                if (PAMM_COMPRESS_USE_GEMM && a.cn2 && gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles)) {
+                    const unsigned pblocks = (unsigned)std::min<int64_t>((a.k + 3) / 4, 1024);
+                    hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
+                    const hipError_t e = hipGetLastError();
+                    if (e != hipSuccess) return e;
                     return launch_compress_gemm<PAMM_COMPRESS_GEMM>(a, ntiles, st);
+                }
+            }
             return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);
     }
 }

@@ -39,6 +39,7 @@ struct CompressArgs {
     float* alpha;
     PartialBest* partial;  // [ntiles x n] when k > kMaxTileGens
     float* xn2;            // [n] when k > kMaxTileGens
+    float* cn2;            // [k] |c_j|^2, bf16 with k > kMaxTileGens / 2 (the GEMM-shaped path)
     int ntiles;            // generator tiles (set by the launcher)
     int num_cus;           // compute units of the device
 };
