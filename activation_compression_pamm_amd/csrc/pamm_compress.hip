@@ -445,6 +445,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     __shared__ __align__(16) char s_tile[2 * TILE];
     __shared__ __align__(16) float s_cn2[BN];
     __shared__ __align__(16) float s_rinv[BN];
+    __shared__ __align__(16) float s_floor[BN];  // score without a valid |c|^2: -1 (padding) or 0
     __shared__ float s_ms[NWC][BM];
     __shared__ int s_mg[NWC][BM];
     __shared__ float s_md[NWC][BM];
@@ -690,6 +691,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         const float v = r < ktile ? a.cn2[gen0 + r] : -1.0f;
         s_cn2[r] = v;
         s_rinv[r] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
+        s_floor[r] = v < 0.f ? -1.0f : 0.f;
     }
     __syncthreads();
     // winners: in passes of 32 rows, each wave writes its 32 x WN block of
@@ -716,11 +718,12 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             const int j0 = wc * WN + sh * (WN / 2) + j;
             const f32x4 cv = *reinterpret_cast<const f32x4*>(s_cn2 + j0);
             const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
+            const f32x4 fv = *reinterpret_cast<const f32x4*>(s_floor + j0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // selects, no branches: a padding generator (|c|^2 = -1)
                 // scores -1 and never wins; |c|^2 = 0 or NaN scores 0
-                const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : (cv[e] < 0.f ? -1.0f : 0.f);
+                const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : fv[e];
                 const bool win = sc > bs;
                 bs = win ? sc : bs;
                 bg = win ? gen0 + j0 + e : bg;
