@@ -781,31 +781,47 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
 }
 
 // Generator pass of the GEMM-shaped path: C = X[gen_idx] and |c_j|^2 (fp32
-// dot2 sums of the stored bf16 values), one wave per generator row.
+// dot2 sums of the stored bf16 values).  One 256-thread workgroup per
+// generator row; each thread issues all its 16-byte chunk loads (up to 8)
+// before using them, so a row costs about one memory round trip.
 __global__ __launch_bounds__(256) void gen_prep_kernel(CompressArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t nw = (int64_t)gridDim.x * 4;
+    constexpr int UNR = 8;
+    __shared__ float s_part[4];
+    const int tid = threadIdx.x;
     const char* __restrict__ X = reinterpret_cast<const char*>(a.X);
     const int64_t row_chunks = (a.d + 7) / 8;
-    for (int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); j < a.k; j += nw) {
+    for (int64_t j = blockIdx.x; j < a.k; j += gridDim.x) {
         int64_t r = a.gen_idx[j];
         r = r < 0 ? 0 : (r >= a.n ? a.n - 1 : r);
         const char* src = X + r * a.ldx_bytes;
         uint16_t* dst = reinterpret_cast<uint16_t*>(a.C) + j * a.d;
-        float s = 0.f;
-        for (int64_t c = lane; c < row_chunks; c += 64) {
-            const uint4 u = load16_tail<DT_BF16>(src, c * 8, a.d);  // zeros past d
-            const v4u32 v = {u.x, u.y, u.z, u.w};
-            s = sumsq_dot2(v, s);
-            if (a.c_vec_ok && c * 8 + 8 <= a.d) {
-                *reinterpret_cast<uint4*>(dst + c * 8) = u;
-            } else {
-                for (int e = 0; e < 8 && c * 8 + e < a.d; ++e) dst[c * 8 + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        float sum = 0.f;
+        for (int64_t c0 = tid; c0 < row_chunks; c0 += 256 * UNR) {
+            uint4 u[UNR];
+#pragma unroll
+            for (int t = 0; t < UNR; ++t) {
+                const int64_t c = c0 + 256 * t;
+                u[t] = c < row_chunks ? load16_tail<DT_BF16>(src, c * 8, a.d) : make_uint4(0, 0, 0, 0);  // zeros past d
+            }
+#pragma unroll
+            for (int t = 0; t < UNR; ++t) {
+                const int64_t c = c0 + 256 * t;
+                const v4u32 v = {u[t].x, u[t].y, u[t].z, u[t].w};
+                sum = sumsq_dot2(v, sum);
+                if (c >= row_chunks) continue;
+                if (a.c_vec_ok && c * 8 + 8 <= a.d) {
+                    *reinterpret_cast<uint4*>(dst + c * 8) = u[t];
+                } else {
+                    for (int e = 0; e < 8 && c * 8 + e < a.d; ++e) dst[c * 8 + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                }
             }
         }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) s += shfl_xor(s, m);
-        if (lane == 0) a.cn2[j] = s;
+        for (int m = 32; m >= 1; m >>= 1) sum += shfl_xor(sum, m);
+        if ((tid & 63) == 0) s_part[tid >> 6] = sum;
+        __syncthreads();
+        if (tid == 0) a.cn2[j] = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+        __syncthreads();
     }
 }
 
@@ -909,7 +925,7 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
         default:
             if constexpr (DT == DT_BF16) {
                 if (PAMM_COMPRESS_USE_GEMM && a.cn2 && gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles)) {
-                    const unsigned pblocks = (unsigned)std::min<int64_t>((a.k + 3) / 4, 1024);
+                    const unsigned pblocks = (unsigned)std::min<int64_t>(a.k, 4096);
                     hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
                     const hipError_t e = hipGetLastError();
                     if (e != hipSuccess) return e;
