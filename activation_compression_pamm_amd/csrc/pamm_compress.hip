@@ -135,11 +135,29 @@ __device__ __forceinline__ void copy_out_generators(const CompressArgs& a, int n
 
 }  // namespace
 
+// Value of lane (l + R) mod 16 within each row of 16 lanes (DPP row_ror; a
+// VALU move, no LDS round trip).
+template <int R, typename T>
+__device__ __forceinline__ T row_ror(T v) {
+    static_assert(sizeof(T) == 4 && R >= 1 && R <= 15, "32-bit value, rotation 1..15");
+    const int x = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(x, x, 0x120 | R, 0xf, 0xf, false));
+}
+
+// One all-reduce round of the (score desc, index asc) winner over 16 lanes.
+template <int R>
+__device__ __forceinline__ void winner_round(float& bs, int& bg, float& bd) {
+    const float os = row_ror<R>(bs);
+    const int og = row_ror<R>(bg);
+    const float od = row_ror<R>(bd);
+    if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = od; }
+}
+
 // Per-row winner among a generator tile, then the eps test and alpha.
 // acc[mt][nt][i] holds S for row 16*mt + 4*(lane/16) + i of the wave and
 // generator 16*nt + lane%16 of the tile; xn2r[mt] holds |x|^2 of row
-// 16*mt + lane%16.  The 16 lanes of a row reduce (score desc, index asc);
-// a NaN score never wins.
+// 16*mt + lane%16.  The 16 lanes of a row reduce (score desc, index asc)
+// by DPP rotations; a NaN score never wins.
 template <int MT, int NTL>
 __device__ __forceinline__ void epilogue_rows(const CompressArgs& a, const f32x4 (&acc)[MT][NTL],
                                               const float (&xn2r)[MT], const float* s_cn2, const float* s_rinv,
@@ -161,13 +179,12 @@ __device__ __forceinline__ void epilogue_rows(const CompressArgs& a, const f32x4
                     if (sc > bs) { bs = sc; bg = gen0 + jl; bd = dot; }
                 }
             }
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-                const float os = shfl_xor(bs, m);
-                const int og = shfl_xor(bg, m);
-                const float od = shfl_xor(bd, m);
-                if (os > bs || (os == bs && og < bg)) { bs = os; bg = og; bd = od; }
-            }
+            // the winner is a maximum under a total order (NaN scores never
+            // enter), so rotations reduce the 16 lanes as well as a butterfly
+            winner_round<8>(bs, bg, bd);
+            winner_round<4>(bs, bg, bd);
+            winner_round<2>(bs, bg, bd);
+            winner_round<1>(bs, bg, bd);
             const float xn2 = __shfl(xn2r[mt], 4 * (lane >> 4) + i, 64);
             const int64_t row = row_base + rloc;
             if ((lane & 15) == i && row < a.n) {
