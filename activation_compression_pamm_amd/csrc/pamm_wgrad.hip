@@ -455,21 +455,44 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
         if (next < nitems) ids(nbegin, ncnt, g, ii, aa);
         begin = nbegin;
         cnt = ncnt;
-        // fixed-order combine of the row groups
+        // fixed-order combine of the row groups; lane g of each group then
+        // stores column g of its PE columns.  With as many groups as columns
+        // (bf16) the combine is a reduce-scatter: at each step a lane keeps
+        // half of its columns and adds the partner's sums for them (7
+        // exchanges instead of 24); otherwise every lane sums all columns.
+        float v;
+        if constexpr (PE == 8 && RG == 8) {
+            const bool h4 = g & 4, h2 = g & 2, h1 = g & 1;
+            float r4[4], r2[2];
 #pragma unroll
-        for (int m = LPR; m < 64; m <<= 1)
+            for (int j = 0; j < 4; ++j) {
+                const float keep = h4 ? acc[4 + j] : acc[j];
+                r4[j] = keep + shfl_xor(h4 ? acc[j] : acc[4 + j], 32);
+            }
 #pragma unroll
-            for (int e = 0; e < PE; ++e) acc[e] += shfl_xor(acc[e], m);
-        // every lane now holds the sums of its PE columns; lane g of the
-        // group stores column g of them straight into the B fragments
-        // (B[n][kk] = P[kk][n]): bf16 lane l, piece 0 holds
-        // B[32nb + l%32][16ks + 8(l/32) + 0..7], split into a hi and a lo
-        // bf16 term (lo blocks after all hi blocks); fp32 lane l, piece h
-        // holds B[32nb + l%32][16ks + 8h + 4(l/32) + 0..3]
-        if (g < PE) {
-            float v = acc[0];
+            for (int j = 0; j < 2; ++j) {
+                const float keep = h2 ? r4[2 + j] : r4[j];
+                r2[j] = keep + shfl_xor(h2 ? r4[j] : r4[2 + j], 16);
+            }
+            // lanes l and l^8 share a row of 16 lanes: a DPP rotation by 8
+            const float send = h1 ? r2[0] : r2[1];
+            const int sx = __builtin_bit_cast(int, send);
+            v = (h1 ? r2[1] : r2[0]) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(sx, sx, 0x128, 0xf, 0xf, false));
+        } else {
+#pragma unroll
+            for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+                for (int e = 0; e < PE; ++e) acc[e] += shfl_xor(acc[e], m);
+            v = acc[0];
 #pragma unroll
             for (int e = 1; e < PE; ++e) v = g == e ? acc[e] : v;
+        }
+        // lane g stores straight into the B fragments (B[n][kk] =
+        // P[kk][n]): bf16 lane l, piece 0 holds B[32nb + l%32][16ks +
+        // 8(l/32) + 0..7], split into a hi and a lo bf16 term (lo blocks
+        // after all hi blocks); fp32 lane l, piece h holds B[32nb +
+        // l%32][16ks + 8h + 4(l/32) + 0..3]
+        if (g < PE) {
             const int64_t n = col + g;
             if (n < a.ncols) {
                 const int64_t nb = n >> 5, ks = ch >> 4;
