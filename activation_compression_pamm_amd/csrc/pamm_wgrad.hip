@@ -45,12 +45,16 @@
 #ifndef PAMM_SR_U
 #define PAMM_SR_U 8
 #endif
-// dW tile of one wave: 32*TM rows x 32*TN columns
+// dW tile of one wave: 32*TM rows x 32*TN columns (32*TN_WIDE columns from
+// kWideProductK generators on)
 #ifndef PAMM_GEMM_TM
 #define PAMM_GEMM_TM 2
 #endif
 #ifndef PAMM_GEMM_TN
 #define PAMM_GEMM_TN 1
+#endif
+#ifndef PAMM_GEMM_TN_WIDE
+#define PAMM_GEMM_TN_WIDE 2
 #endif
 
 namespace pamm {
@@ -707,6 +711,26 @@ WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out) {
     return L;
 }
 
+// Generator counts from which the product uses the wider wave tile.
+constexpr int kWideProductK = 256;
+
+template <int DT, int TM, int TN>
+static void launch_gen_gemm(const GemmArgs& g, const WgradArgs& a, hipStream_t st) {
+    const int64_t waves = ((a.d + 32 * TM - 1) / (32 * TM)) * ((a.d_out + 32 * TN - 1) / (32 * TN));
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (a.transpose_out) {
+        if (a.accumulate)
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, TM, TN, true, true>), grid, dim3(256), 0, st, g);
+        else
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, TM, TN, false, true>), grid, dim3(256), 0, st, g);
+    } else {
+        if (a.accumulate)
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, TM, TN, true, false>), grid, dim3(256), 0, st, g);
+        else
+            hipLaunchKernelGGL((gen_gemm_kernel<DT, TM, TN, false, false>), grid, dim3(256), 0, st, g);
+    }
+}
+
 template <int DT>
 static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     const WgradLayout& L = a.L;
@@ -769,23 +793,15 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     GemmArgs g;
     g.AF = ws + L.off_AT; g.BF = ws + L.off_BT; g.ks_cap = L.ks_cap; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks;
     g.dW = a.dW; g.lddw = a.lddw;
-    const int64_t waves = ((a.d + 32 * PAMM_GEMM_TM - 1) / (32 * PAMM_GEMM_TM)) *
-                          ((a.d_out + 32 * PAMM_GEMM_TN - 1) / (32 * PAMM_GEMM_TN));
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    if (a.transpose_out) {
-        if (a.accumulate)
-            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, true, true>), grid, dim3(256), 0, st, g);
-        else
-            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, false, true>), grid, dim3(256), 0, st,
-                               g);
-    } else {
-        if (a.accumulate)
-            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, true, false>), grid, dim3(256), 0, st,
-                               g);
-        else
-            hipLaunchKernelGGL((gen_gemm_kernel<DT, PAMM_GEMM_TM, PAMM_GEMM_TN, false, false>), grid, dim3(256), 0, st,
-                               g);
-    }
+    // With k >= kWideProductK the contraction has at least as many chunk
+    // steps and the product reads its operands from L2 many times over: a
+    // wider wave tile (64 x 64) halves that traffic.  With few steps the
+    // product is bound by the dW write, and the narrower tile (64 x 32)
+    // spreads the stores over more waves.
+    if (a.k >= kWideProductK)
+        launch_gen_gemm<DT, PAMM_GEMM_TM, PAMM_GEMM_TN_WIDE>(g, a, st);
+    else
+        launch_gen_gemm<DT, PAMM_GEMM_TM, PAMM_GEMM_TN>(g, a, st);
     return hipGetLastError();
 }
 

@@ -22,9 +22,10 @@ def say(*a):
     sys.stdout.flush()
 
 
+@pytest.mark.parametrize("k", [40, 300])   # 300: the wide product tile
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_transposed_output_is_the_transpose(dtype):
-    n, d, dout, k = 3000, 200, 296, 40
+def test_transposed_output_is_the_transpose(dtype, k):
+    n, d, dout = 3000, 200, 296
     say("transpose_out", dtype, f"n={n} d={d} d_out={dout} k={k}")
     X = synth.clustered_activations(n, d, 16, seed=5, dtype=dtype)
     dY = synth.gradients(n, dout, seed=6, dtype=dtype)
