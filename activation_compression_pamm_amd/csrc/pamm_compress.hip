@@ -444,7 +444,9 @@ __device__ __forceinline__ float sumsq_dot2(const v4u32& v, float acc) {
     return acc;
 }
 
-template <int MT, int NT, int NWR, int NWC>
+// MASKED: the tail stage and padding positions exist (d not a multiple of 64,
+// or an odd stage count); without them the stash applies no masks.
+template <int MT, int NT, int NWR, int NWC, bool MASKED>
 __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressArgs a) {
     constexpr int RB = 128;                 // bytes of a row per stage
     constexpr int E = RB / 2;               // elements per stage
@@ -565,14 +567,14 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         if (part < 2) {
 #pragma unroll
             for (int i = 4 * part; i < 4 * part + 4; ++i) {
-                const v4u32 v = xr[i] & m;
+                const v4u32 v = MASKED ? xr[i] & m : xr[i];
                 *reinterpret_cast<v4u32*>(buf + dst0 + i * (NTH / 8) * RB) = v;
                 if constexpr (decltype(wx)::value) xsq[i] = sumsq_dot2(v, xsq[i]);
             }
         } else {
 #pragma unroll
             for (int i = 4 * (part - 2); i < 4 * (part - 2) + 4; ++i)
-                *reinterpret_cast<v4u32*>(buf + BM * RB + dst0 + i * (NTH / 8) * RB) = cr[i] & m;
+                *reinterpret_cast<v4u32*>(buf + BM * RB + dst0 + i * (NTH / 8) * RB) = MASKED ? cr[i] & m : cr[i];
         }
     };
     auto stash = [&](int p, char* buf, auto wx) __attribute__((always_inline)) {
@@ -882,10 +884,14 @@ static hipError_t launch_compress_rs(const CompressArgs& a, int ntiles, hipStrea
 
 template <int MT, int NT, int NWR, int NWC>
 static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStream_t st) {
-    constexpr int BM = 16 * MT * NWR;
+    constexpr int BM = 32 * MT * NWR;
     const int64_t nrb = (a.n + BM - 1) / BM;
     const dim3 grid((unsigned)(ntiles > 1 ? (nrb + 7) / 8 * 8 * ntiles : nrb));
-    hipLaunchKernelGGL((compress_gemm_kernel<MT, NT, NWR, NWC>), grid, dim3(64 * NWR * NWC), 0, st, a);
+    const int64_t nst = (a.d + 63) / 64;
+    if (a.d % 64 != 0 || nst % 2 != 0)
+        hipLaunchKernelGGL((compress_gemm_kernel<MT, NT, NWR, NWC, true>), grid, dim3(64 * NWR * NWC), 0, st, a);
+    else
+        hipLaunchKernelGGL((compress_gemm_kernel<MT, NT, NWR, NWC, false>), grid, dim3(64 * NWR * NWC), 0, st, a);
     return hipGetLastError();
 }
 
