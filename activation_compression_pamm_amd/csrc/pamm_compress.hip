@@ -535,8 +535,10 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // for parts 2-3) of position p into registers
     auto issue_part = [&](int p, int part) __attribute__((always_inline)) {
         const int st = stage_of(p);
-        // chunks past the row end (tail stage) re-read the row's last chunk
-        const uint32_t q16 = (uint32_t)min((int64_t)qc, row_chunks - 1 - (int64_t)st * (RB / 16)) * 16u;
+        // chunks past the row end (tail stage) re-read the row's last chunk;
+        // without a tail stage the chunk offset is the same every stage
+        const uint32_t q16 =
+            MASKED ? (uint32_t)min((int64_t)qc, row_chunks - 1 - (int64_t)st * (RB / 16)) * 16u : (uint32_t)qc * 16u;
         if (part < 2) {
             const char* bx = X + m0 * a.ldx_bytes + (int64_t)st * RB;
 #pragma unroll
