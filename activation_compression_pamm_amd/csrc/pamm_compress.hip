@@ -407,6 +407,30 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     epilogue_rows<MT, NTL>(a, acc, xn2r, s_cn2, s_rinv, m0 + wave * WM, tile, gen0, ktile, lane);
 }
 
+// Requested instruction order for one scheduling region of the GEMM-shaped
+// kernel's loop: each LDS read, LDS write and global load is issued right
+// after one of the region's MFMAs (NR reads first, then NW writes, then NV
+// loads; NM MFMAs left over), so that it issues while the MFMA runs.  Left to
+// itself the scheduler clusters them between runs of MFMAs, and the matrix
+// core idles while they issue and while the LDS writes wait for their data.
+template <int NR, int NW, int NV, int NM>
+__device__ __forceinline__ void interleave_region() {
+    static_for<0, NR>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    static_for<0, NW>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); });
+    static_for<0, NV>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); });
+    if constexpr (NM > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+}
+// The same with NR reads first, then NP pairs of (LDS write, global load).
+template <int NR, int NP>
+__device__ __forceinline__ void interleave_region2() {
+    static_for<0, NR>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    static_for<0, NP>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    });
+}
+
 // Tiles of 256 generators in bf16: the contraction dominates (k >= 256 means
 // at least 256 MFMA flops per byte of X), so the workgroup is shaped like a
 // GEMM tile: NWR x NWC waves, each holding 32*MT rows x 32*NT generators of
@@ -634,11 +658,13 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         mfma_step(xa, ca);                     // step 0 (read before the last barrier)
         stash_part(m, nxt, 0, wx);
         issue_part(pf, 0);
+        interleave_region<MT + NT, 4, 4, MT * NT - (MT + NT) - 8>();
         fence();
         load_frags(cur, 2, xa, ca);
         mfma_step(xb, cb);                     // step 1
         stash_part(m, nxt, 1, wx);
         issue_part(pf, 1);
+        interleave_region<MT + NT, 4, 4, MT * NT - (MT + NT) - 8>();
         fence();
         load_frags(cur, 3, xb, cb);
         mfma_step(xa, ca);                     // step 2
@@ -646,12 +672,14 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         issue_part(pf, 2);
         stash_part(m, nxt, 3, wx);
         issue_part(pf, 3);
+        interleave_region2<MT + NT, 8>();
         fence();
         wait_lds();
         ring_barrier();
         fence();
         load_frags(nxt, 0, xa, ca);            // step 0 of position p+1
         mfma_step(xb, cb);                     // step 3
+        interleave_region<MT + NT, 0, 0, MT * NT - (MT + NT)>();
         fence();
     };
     auto tail = [&](const char* cur) __attribute__((always_inline)) {
@@ -667,6 +695,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         mfma_step(xb, cb);
     };
     static_assert(E / 16 == 4, "the skewed schedule is written for four K steps per stage");
+    static_assert(MT * NT >= MT + NT + 8, "each region's memory instructions need an MFMA each");
 
     // the main loop, in two versions: with |x|^2 (first generator tile) or
     // without (the other tiles; their |x|^2 would be the same)
@@ -707,50 +736,37 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         for (int q = 0; q < 8; ++q) v += ring[r * 8 + q];
         s_xn2[r] = v;
     }
+    int plain_gen = 1;
     for (int r = tid; r < BN; r += NTH) {
         // a padding generator of a partial tile is marked by |c|^2 = -1
         const float v = r < ktile ? a.cn2[gen0 + r] : -1.0f;
         s_cn2[r] = v;
         s_rinv[r] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
         s_floor[r] = v < 0.f ? -1.0f : 0.f;
+        plain_gen &= v > 0.f && v < INFINITY;
     }
-    __syncthreads();
+    // tiles whose generators all have a finite, positive |c|^2 (no zero,
+    // NaN or infinite norm, no padding) take the shorter scan below
+    const bool plain = __syncthreads_and(plain_gen);
     // winners: in passes of 32 rows, each wave writes its 32 x WN block of
     // S row-major (rows padded by 4 floats against bank conflicts); two lanes
     // per row then scan WN/2 generators each in increasing order (lowest
     // index on ties, NaN never wins) and the pair is merged.  Element i of a
     // 32x32 result lane l is row 8*(i/4) + 4*(l/32) + i%4, generator l%32.
     constexpr int PST = WN + 4;  // floats per staged row
+    constexpr int HW = WN / 2;   // generators scanned per lane
     float* wbuf = ring + wave * 32 * PST;
     const int sr = lane >> 1, sh = lane & 1;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    const int jl0 = wc * WN + sh * HW;  // tile index of the lane's first generator
+    const float* rowp = wbuf + sr * PST + sh * HW;
+    auto stage_rows = [&](int mt) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 wbuf[(8 * (i >> 2) + 4 * fk + (i & 3)) * PST + nt * 32 + frow] = acc[mt][nt][i];
-        float bs = -1.0f, bd = 0.f;
-        int bg = 0x7fffffff;
-        const float* rowp = wbuf + sr * PST + sh * (WN / 2);
-#pragma unroll
-        for (int j = 0; j < WN / 2; j += 4) {
-            const f32x4 dv = *reinterpret_cast<const f32x4*>(rowp + j);
-            const int j0 = wc * WN + sh * (WN / 2) + j;
-            const f32x4 cv = *reinterpret_cast<const f32x4*>(s_cn2 + j0);
-            const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
-            const f32x4 fv = *reinterpret_cast<const f32x4*>(s_floor + j0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // selects, no branches: a padding generator (|c|^2 = -1)
-                // scores -1 and never wins; |c|^2 = 0 or NaN scores 0
-                const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : fv[e];
-                const bool win = sc > bs;
-                bs = win ? sc : bs;
-                bg = win ? gen0 + j0 + e : bg;
-                bd = win ? dv[e] : bd;
-            }
-        }
+    };
+    auto publish = [&](int mt, float bs, int bg, float bd) __attribute__((always_inline)) {
         const float os = shfl_xor(bs, 1);
         const int og = shfl_xor(bg, 1);
         const float od = shfl_xor(bd, 1);
@@ -763,6 +779,62 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             s_ms[wc][rloc] = bs;
             s_mg[wc][rloc] = bg;
             s_md[wc][rloc] = bd;
+        }
+    };
+    if (plain) {
+        // score = |S| / |c| with 1/|c| of the lane's generators in registers;
+        // only the winner's position is tracked, its S is read back after
+        float w[HW];
+#pragma unroll
+        for (int j = 0; j < HW; j += 4) {
+            const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + jl0 + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[j + e] = rv[e];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            stage_rows(mt);
+            float bs = -1.0f;
+            int bj = -1;
+#pragma unroll
+            for (int j = 0; j < HW; j += 4) {
+                const f32x4 dv = *reinterpret_cast<const f32x4*>(rowp + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sc = fabsf(dv[e]) * w[j + e];
+                    const bool win = sc > bs;  // false for NaN
+                    bs = win ? sc : bs;
+                    bj = win ? j + e : bj;
+                }
+            }
+            const float bd = rowp[bj < 0 ? 0 : bj];
+            publish(mt, bs, bj < 0 ? 0x7fffffff : gen0 + jl0 + bj, bj < 0 ? 0.f : bd);
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            stage_rows(mt);
+            float bs = -1.0f, bd = 0.f;
+            int bg = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < HW; j += 4) {
+                const f32x4 dv = *reinterpret_cast<const f32x4*>(rowp + j);
+                const int j0 = jl0 + j;
+                const f32x4 cv = *reinterpret_cast<const f32x4*>(s_cn2 + j0);
+                const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
+                const f32x4 fv = *reinterpret_cast<const f32x4*>(s_floor + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // selects, no branches: a padding generator (|c|^2 = -1)
+                    // scores -1 and never wins; |c|^2 = 0 or NaN scores 0
+                    const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : fv[e];
+                    const bool win = sc > bs;
+                    bs = win ? sc : bs;
+                    bg = win ? gen0 + j0 + e : bg;
+                    bd = win ? dv[e] : bd;
+                }
+            }
+            publish(mt, bs, bg, bd);
         }
     }
     __syncthreads();

@@ -261,6 +261,36 @@ def test_gemm_tiles_degenerate_rows():
         check_compress(X, g, eps, to_host(C), f_g, a_g)
 
 
+def test_gemm_tiles_degenerate_rows_plain_generators():
+    # the same rows with every generator of finite, positive norm (no zero
+    # generator, no padding): the epilogue's shorter scan
+    n, d, k = 65536, 128, 256
+    X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 35, "bf16")).copy()
+    X32[40] = X32[7]
+    X32[41] = -4 * X32[7]
+    X32[101] = 0.0
+    X32[102, 5] = np.nan
+    X = synth.f32_to_bf16_bits(X32)
+    rng = np.random.default_rng(36)
+    others = rng.choice(np.setdiff1d(np.arange(n), [7, 40, 41, 101, 102]), k - 2, replace=False)
+    g = np.sort(np.concatenate([[7, 40], others])).astype(np.int32)
+    s7 = int(np.searchsorted(g, 7))
+    gd = torch.from_numpy(g).cuda()
+    for eps in (0.0, 0.2):
+        say("gemm-degenerate-plain", eps)
+        C, f, a = pamm.compress(to_dev(X), gd, eps)
+        torch.cuda.synchronize()
+        f_g, a_g = to_host(f), to_host(a)
+        assert f_g[7] == s7 and f_g[40] == s7 and f_g[41] == s7
+        assert abs(a_g[41] + 4.0) <= 4.0 * 1e-5 and a_g[7] == a_g[40]
+        assert f_g[102] == -1 and a_g[102] == 0.0
+        if eps == 0.0:
+            assert f_g[101] == 0 and a_g[101] == 0.0   # all scores 0: the lowest slot
+        else:
+            assert f_g[101] == -1
+        check_compress(X, g, eps, to_host(C), f_g, a_g)
+
+
 def test_no_generators_and_single_row():
     X = synth.random_matrix(50, 16, 41, "bf16")
     dY = synth.random_matrix(50, 24, 42, "bf16")
