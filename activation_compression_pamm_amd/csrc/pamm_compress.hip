@@ -92,6 +92,14 @@ __device__ __forceinline__ int swz(int r, int q) {
     return r * RB + ((q ^ (r & (RB / 16 - 1))) << 4);
 }
 
+// Swizzle key of the GEMM-shaped kernel's 128-byte rows, whose 32x32x16
+// fragment reads take rows l%32 at chunk 2k + l/32.  Chosen by measurement
+// (SQ_LDS_BANK_CONFLICT against SQ_LDS_IDX_ACTIVE): with the key r%8 a third
+// of that kernel's LDS-active cycles were bank-conflict stalls, with this key
+// under 4%.  The 16x16x32 reads of compress_rs_kernel (rows l%16 at chunk
+// 4k + l/16) are conflict-free with r%8 and conflict with this key.
+__device__ __forceinline__ int gemm_swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // Call f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -536,9 +544,9 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         g = g < 0 ? 0 : (g >= a.n ? a.n - 1 : g);
         coff[i] = (uint32_t)(g * a.ldx_bytes);
     }
-    // LDS slot of load i: row (NTH/8)*i + rsub, chunk qc, swizzled by row%8
-    // (the same for every i, so slot i is slot 0 plus a constant)
-    const int dst0 = swz<RB>(rsub, qc);
+    // LDS slot of load i: row (NTH/8)*i + rsub, chunk qc swizzled by the
+    // row's key (the same for every i, so slot i is slot 0 plus a constant)
+    const int dst0 = rsub * RB + ((qc ^ gemm_swz_key(rsub)) << 4);
     // stage at position p: workgroups start at different column ranges (as
     // above); positions past the last stage re-read it and are zeroed
     const int rot = PAMM_COMPRESS_ROTATE ? (int)(((uint64_t)rb * 37u) % (unsigned)nst) : 0;
@@ -617,12 +625,12 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
 
     // fragment of 32x32x16: lane l holds row l%32 of the 32-row tile and
     // elements 8*(l/32) .. +7 of the 16-element K step.  Every tile row the
-    // lane reads has row%8 = l%8, so a fragment's LDS address is one base per
-    // K step (the chunk swizzle) plus compile-time offsets.
+    // lane reads has row%32 = l%32, hence the same swizzle key, so a
+    // fragment's LDS address is one base per K step plus compile-time offsets.
     const int frow = lane & 31, fk = lane >> 5;
     int fa[E / 16];
 #pragma unroll
-    for (int ks = 0; ks < E / 16; ++ks) fa[ks] = frow * RB + ((((2 * ks + fk) ^ (frow & 7))) << 4);
+    for (int ks = 0; ks < E / 16; ++ks) fa[ks] = frow * RB + (((2 * ks + fk) ^ gemm_swz_key(frow)) << 4);
     const int xw = wr * WM * RB, cw = BM * RB + wc * WN * RB;
     auto load_frags = [&](const char* buf, int ks, v4u32 (&xf)[MT], v4u32 (&cf)[NT]) __attribute__((always_inline)) {
         const char* bx = buf + xw + fa[ks];
@@ -749,22 +757,26 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // NaN or infinite norm, no padding) take the shorter scan below
     const bool plain = __syncthreads_and(plain_gen);
     // winners: in passes of 32 rows, each wave writes its 32 x WN block of
-    // S row-major (rows padded by 4 floats against bank conflicts); two lanes
+    // S row-major (rows padded against bank conflicts); two lanes
     // per row then scan WN/2 generators each in increasing order (lowest
     // index on ties, NaN never wins) and the pair is merged.  Element i of a
     // 32x32 result lane l is row 8*(i/4) + 4*(l/32) + i%4, generator l%32.
-    constexpr int PST = WN + 4;  // floats per staged row
-    constexpr int HW = WN / 2;   // generators scanned per lane
+    // Each staged row holds the lane pair's two halves 4 floats apart from
+    // a multiple of the bank count, so the pair's reads use different banks.
+    constexpr int HW = WN / 2;         // generators scanned per lane
+    constexpr int HOFF = HW + 4;       // offset of the second half
+    constexpr int PST = WN + 8;        // floats per staged row
     float* wbuf = ring + wave * 32 * PST;
     const int sr = lane >> 1, sh = lane & 1;
     const int jl0 = wc * WN + sh * HW;  // tile index of the lane's first generator
-    const float* rowp = wbuf + sr * PST + sh * HW;
+    const float* rowp = wbuf + sr * PST + sh * HOFF;
     auto stage_rows = [&](int mt) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                wbuf[(8 * (i >> 2) + 4 * fk + (i & 3)) * PST + nt * 32 + frow] = acc[mt][nt][i];
+                wbuf[(8 * (i >> 2) + 4 * fk + (i & 3)) * PST + nt * 32 + frow + (nt * 32 >= HW ? HOFF - HW : 0)] =
+                    acc[mt][nt][i];
     };
     auto publish = [&](int mt, float bs, int bg, float bd) __attribute__((always_inline)) {
         const float os = shfl_xor(bs, 1);
