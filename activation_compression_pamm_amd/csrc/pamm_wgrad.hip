@@ -411,54 +411,87 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
         bg = c < nch ? a.chunk_begin[c] : 0;
         cn = c < nch ? a.chunk_count[c] : 0;
     };
-    auto ids = [&](int bg, int cn, int t0, int* ii, float* aa) {
+    auto row_ids = [&](int bg, int cn, int t0, int* ii) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int tt = t0 + RG * u;
             ii[u] = tt < cn ? a.perm[bg + tt] : -1;
+        }
+    };
+    auto row_alphas = [&](int bg, int cn, int t0, float* aa) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tt = t0 + RG * u;
             aa[u] = tt < cn ? a.palpha[bg + tt] : 0.f;
         }
     };
-    // the chunk list entry and the first batch's row ids of the wave's next
-    // item are fetched while the current item streams its dY rows
-    int begin = 0, cnt = 0;
-    int ii[U];
+    // dY pieces of rows ii at the item's column slab (read once: non-temporal
+    // loads of whole 16-byte groups)
+    auto fetch = [&](int64_t it, const int* ii, uint4* vv) __attribute__((always_inline)) {
+        const int64_t col = (it % a.nslab) * SC + lq * PE;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            vv[u] = ii[u] < 0 ? make_uint4(0, 0, 0, 0)
+                    : (col + PE <= a.d_out
+                           ? load16_nt(a.dY + (int64_t)ii[u] * a.lddy_bytes + col * Elem<DT>::size)
+                           : load16_tail<DT>(a.dY + (int64_t)ii[u] * a.lddy_bytes, col, a.d_out));
+    };
+    auto accumulate = [&](const uint4* vv, const float* aa, float* acc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[PE];
+            unpack16<DT>(vv[u], v);
+#pragma unroll
+            for (int e = 0; e < PE; ++e) acc[e] = __builtin_fmaf(aa[u], v[e], acc[e]);
+        }
+    };
+    // Software pipeline over the wave's items (stride wstride): while item i
+    // is combined and stored, the dY pieces of item i+1's first batch are in
+    // flight, the row ids of item i+2's first batch are being fetched and
+    // the chunk list entry of item i+3.  Later batches of a long chunk are
+    // fetched in turn.
+    int b0 = 0, c0 = 0, b1 = 0, c1 = 0, b2 = 0, c2 = 0;
+    int jj[U];
     float aa[U];
+    uint4 vv[U];
     if (wave < nitems) {
-        meta(wave, begin, cnt);
-        ids(begin, cnt, g, ii, aa);
+        meta(wave, b0, c0);
+        int ii[U];
+        row_ids(b0, c0, g, ii);
+        row_alphas(b0, c0, g, aa);
+        fetch(wave, ii, vv);
     }
+    if (wave + wstride < nitems) {
+        meta(wave + wstride, b1, c1);
+        row_ids(b1, c1, g, jj);
+    }
+    if (wave + 2 * wstride < nitems) meta(wave + 2 * wstride, b2, c2);
     for (int64_t item = wave; item < nitems; item += wstride) {
-        const int64_t next = item + wstride;
-        int nbegin = 0, ncnt = 0;
-        if (next < nitems) meta(next, nbegin, ncnt);
         const int64_t ch = item / a.nslab;
         const int64_t col = (item % a.nslab) * SC + lq * PE;
         float acc[PE];
 #pragma unroll
         for (int e = 0; e < PE; ++e) acc[e] = 0.f;
-        const int nbatch = (cnt + 63) >> 6;
-        for (int bt = 0; bt < nbatch; ++bt) {
-            if (bt > 0) ids(begin, cnt, g + 64 * bt, ii, aa);
-            uint4 vv[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-            // dY rows are read once: non-temporal loads for whole 16-byte groups
-                vv[u] = ii[u] < 0 ? make_uint4(0, 0, 0, 0)
-                        : (col + PE <= a.d_out
-                               ? load16_nt(a.dY + (int64_t)ii[u] * a.lddy_bytes + col * Elem<DT>::size)
-                               : load16_tail<DT>(a.dY + (int64_t)ii[u] * a.lddy_bytes, col, a.d_out));
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float v[PE];
-                unpack16<DT>(vv[u], v);
-#pragma unroll
-                for (int e = 0; e < PE; ++e) acc[e] = __builtin_fmaf(aa[u], v[e], acc[e]);
-            }
+        accumulate(vv, aa, acc);  // first batch, fetched ahead
+        const int nbatch = (c0 + 63) >> 6;
+        for (int bt = 1; bt < nbatch; ++bt) {
+            int ii[U];
+            row_ids(b0, c0, g + 64 * bt, ii);
+            row_alphas(b0, c0, g + 64 * bt, aa);
+            fetch(item, ii, vv);
+            accumulate(vv, aa, acc);
         }
-        if (next < nitems) ids(nbegin, ncnt, g, ii, aa);
-        begin = nbegin;
-        cnt = ncnt;
+        const int64_t n1 = item + wstride, n2 = n1 + wstride, n3 = n2 + wstride;
+        if (n1 < nitems) {
+            fetch(n1, jj, vv);
+            row_alphas(b1, c1, g, aa);
+        }
+        if (n2 < nitems) row_ids(b2, c2, g, jj);
+        int b3 = 0, c3 = 0;
+        if (n3 < nitems) meta(n3, b3, c3);
+        b0 = b1; c0 = c1;
+        b1 = b2; c1 = c2;
+        b2 = b3; c2 = c3;
         // fixed-order combine of the row groups; lane g of each group then
         // stores column g of its PE columns.  With as many groups as columns
         // (bf16) the combine is a reduce-scatter: at each step a lane keeps
