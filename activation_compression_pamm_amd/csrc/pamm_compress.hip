@@ -708,6 +708,13 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // the main loop, in two versions: with |x|^2 (first generator tile) or
     // without (the other tiles; their |x|^2 would be the same)
     auto run = [&](auto wx) __attribute__((always_inline)) {
+        // distinct empty statements with a memory clobber open the two
+        // versions: without them the compiler hoists their identical first
+        // loads above the branch and spills the staged lines across it
+        if constexpr (decltype(wx)::value)
+            asm volatile("; norms" ::: "memory");
+        else
+            asm volatile("; no norms" ::: "memory");
         issue(0);
         stash(0, s_tile, wx);
         issue(1);
