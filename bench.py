@@ -10,6 +10,11 @@ with every input resident in HBM before timing starts.  Two input batches
 alternate so that no step finds its inputs in the memory-side cache.
 Generator sets for all steps are drawn on the host beforehand and uploaded.
 
+The default times 2000 steps (about 0.3 s): under this load the core clock
+dips for the first few milliseconds after the GPU leaves idle and recovers
+after about a hundred steps, so a window of 100 steps reads mostly the dip
+(about 9% fewer tokens/s) while a long-running job sees the steady state.
+
 Prints one JSON line: tokens/s for the whole job, per-call times, a roofline
 entry for the dominant kernel (HIP events around its launches on the stream
 it runs on) and the CPU oracle timed on a bounded sample of the same
@@ -42,8 +47,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_llama7b_qkv_traffic.json
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="llama7b_qkv")
     p.add_argument("--sample-every", type=int, default=10,
                    help="record per-call HIP events on every this many'th timed step")
