@@ -446,10 +446,13 @@ __device__ __forceinline__ void interleave_region2() {
 // accumulation register file), so one LDS fragment read feeds 4 MFMAs.
 //   * One stage = 64 elements (128 bytes) of every tile row.  X and C lines
 //     are fetched as whole 128-byte lines into registers one stage ahead and
-//     written to a double-buffered, XOR-swizzled LDS tile (as above).  The
-//     steady-state loop has no branch: the stage count is padded to an even
-//     number, and padding stages and the columns past d are masked to zero
-//     on their way into LDS.
+//     written to a double-buffered LDS tile, XOR-swizzled with this kernel's
+//     own key (gemm_swz_key).  The steady-state loop has no branch: the stage
+//     count is padded to an even number, and padding stages and the columns
+//     past d are masked to zero on their way into LDS (a second instance
+//     without masks serves d a multiple of 64 with an even stage count).
+//     Within each scheduling region every memory instruction is issued right
+//     after one MFMA (interleave_region).
 //   * |x_i|^2 is summed in fp32 with bf16 dot2 instructions from the staged
 //     lines by the workgroups of the first generator tile; |c_j|^2 likewise,
 //     once per generator, by gen_prep_kernel, which also writes C.  (The
