@@ -439,6 +439,23 @@ __device__ __forceinline__ void interleave_region2() {
     });
 }
 
+// The same for regions with more memory instructions than MFMAs: the NR
+// reads, NW writes and NV loads, in that order, are spread evenly over the
+// NM MFMAs (MFMA i is followed by instructions NO*i/NM .. NO*(i+1)/NM - 1).
+template <int NR, int NW, int NV>
+__device__ __forceinline__ constexpr int op_mask(int o) { return o < NR ? 0x100 : (o < NR + NW ? 0x200 : 0x020); }
+template <int NR, int NW, int NV, int NM>
+__device__ __forceinline__ void interleave_spread() {
+    constexpr int NO = NR + NW + NV;
+    static_for<0, NM>([&](auto mi) {
+        constexpr int i = decltype(mi)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        static_for<NO * i / NM, NO * (i + 1) / NM>([&](auto oi) {
+            __builtin_amdgcn_sched_group_barrier(op_mask<NR, NW, NV>(decltype(oi)::value), 1, 0);
+        });
+    });
+}
+
 // Tiles of 256 generators in bf16: the contraction dominates (k >= 256 means
 // at least 256 MFMA flops per byte of X), so the workgroup is shaped like a
 // GEMM tile: NWR x NWC waves, each holding 32*MT rows x 32*NT generators of
@@ -558,7 +575,10 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     auto valid_elems = [&](int p) { return p >= nst ? 0 : (stage_of(p) == last ? tail_elems : E); };
     const int64_t row_chunks = (a.row_bytes + 15) / 16;
 
-    static_assert(XPT == 8 && CPT == 8, "the stash is split in four parts of four chunks");
+    // the staged lines of a lane are handled in parts of four chunks: XP
+    // parts of X, then CP parts of C
+    constexpr int XP = XPT / 4, CP = CPT / 4, NP = XP + CP;
+    static_assert(XPT % 4 == 0 && CPT % 4 == 0 && NP >= 3 && NP <= 4, "the stash is split in three or four parts");
     v4u32 xr[XPT], cr[CPT];
     // per-lane partial |x|^2 of the rows this lane fetches (summed by the
     // workgroups of the first generator tile only; |c|^2 comes from the
@@ -574,20 +594,20 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         // without a tail stage the chunk offset is the same every stage
         const uint32_t q16 =
             MASKED ? (uint32_t)min((int64_t)qc, row_chunks - 1 - (int64_t)st * (RB / 16)) * 16u : (uint32_t)qc * 16u;
-        if (part < 2) {
+        if (part < XP) {
             const char* bx = X + m0 * a.ldx_bytes + (int64_t)st * RB;
 #pragma unroll
             for (int i = 4 * part; i < 4 * part + 4; ++i) xr[i] = *reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16));
         } else {
             const char* bc = X + (int64_t)st * RB;
 #pragma unroll
-            for (int i = 4 * (part - 2); i < 4 * (part - 2) + 4; ++i)
+            for (int i = 4 * (part - XP); i < 4 * (part - XP) + 4; ++i)
                 cr[i] = *reinterpret_cast<const v4u32*>(bc + (coff[i] + q16));
         }
     };
     auto issue = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-        for (int part = 0; part < 4; ++part) issue_part(p, part);
+        for (int part = 0; part < NP; ++part) issue_part(p, part);
     };
     // registers of position p -> an LDS buffer.  Elements at or past the
     // position's valid count (the tail stage's columns past d, all of a
@@ -601,7 +621,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         return m;
     };
     auto stash_part = [&](const v4u32& m, char* buf, int part, auto wx) __attribute__((always_inline)) {
-        if (part < 2) {
+        if (part < XP) {
 #pragma unroll
             for (int i = 4 * part; i < 4 * part + 4; ++i) {
                 const v4u32 v = MASKED ? xr[i] & m : xr[i];
@@ -610,14 +630,14 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             }
         } else {
 #pragma unroll
-            for (int i = 4 * (part - 2); i < 4 * (part - 2) + 4; ++i)
+            for (int i = 4 * (part - XP); i < 4 * (part - XP) + 4; ++i)
                 *reinterpret_cast<v4u32*>(buf + BM * RB + dst0 + i * (NTH / 8) * RB) = MASKED ? cr[i] & m : cr[i];
         }
     };
     auto stash = [&](int p, char* buf, auto wx) __attribute__((always_inline)) {
         const v4u32 m = stage_mask(p);
 #pragma unroll
-        for (int part = 0; part < 4; ++part) stash_part(m, buf, part, wx);
+        for (int part = 0; part < NP; ++part) stash_part(m, buf, part, wx);
     };
 
     f32x16 acc[MT][NT];
@@ -662,6 +682,22 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // sched_barrier(0) fences keep the compiler from moving work across.
     v4u32 xa[MT], ca[NT], xb[MT], cb[NT];
     auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    // requested orders: one memory instruction per MFMA where there are
+    // enough MFMAs, else the instructions spread evenly over them
+    constexpr int NMF = MT * NT, NRD = MT + NT, NCS = 4 * (NP - 2);  // NCS: chunks staged in region 3
+    auto order_part = [&]() __attribute__((always_inline)) {       // regions 1 and 2
+        if constexpr (NMF >= NRD + 8) interleave_region<NRD, 4, 4, NMF - NRD - 8>();
+        else interleave_spread<NRD, 4, 4, NMF>();
+    };
+    auto order_last_parts = [&]() __attribute__((always_inline)) {  // region 3
+        if constexpr (NCS == 8 && NMF >= NRD + 8) interleave_region2<NRD, 8>();
+        else if constexpr (NMF >= NRD + 2 * NCS) interleave_region<NRD, NCS, NCS, NMF - NRD - 2 * NCS>();
+        else interleave_spread<NRD, NCS, NCS, NMF>();
+    };
+    auto order_reads = [&]() __attribute__((always_inline)) {       // region 4
+        if constexpr (NMF >= NRD) interleave_region<NRD, 0, 0, NMF - NRD>();
+        else interleave_spread<NRD, 0, 0, NMF>();
+    };
     auto body = [&](int p, const char* cur, char* nxt, auto wx) __attribute__((always_inline)) {
         const v4u32 m = stage_mask(p + 1);
         const int pf = min(p + 2, npos - 1);
@@ -669,28 +705,29 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         mfma_step(xa, ca);                     // step 0 (read before the last barrier)
         stash_part(m, nxt, 0, wx);
         issue_part(pf, 0);
-        interleave_region<MT + NT, 4, 4, MT * NT - (MT + NT) - 8>();
+        order_part();
         fence();
         load_frags(cur, 2, xa, ca);
         mfma_step(xb, cb);                     // step 1
         stash_part(m, nxt, 1, wx);
         issue_part(pf, 1);
-        interleave_region<MT + NT, 4, 4, MT * NT - (MT + NT) - 8>();
+        order_part();
         fence();
         load_frags(cur, 3, xb, cb);
         mfma_step(xa, ca);                     // step 2
-        stash_part(m, nxt, 2, wx);
-        issue_part(pf, 2);
-        stash_part(m, nxt, 3, wx);
-        issue_part(pf, 3);
-        interleave_region2<MT + NT, 8>();
+#pragma unroll
+        for (int part = 2; part < NP; ++part) {
+            stash_part(m, nxt, part, wx);
+            issue_part(pf, part);
+        }
+        order_last_parts();
         fence();
         wait_lds();
         ring_barrier();
         fence();
         load_frags(nxt, 0, xa, ca);            // step 0 of position p+1
         mfma_step(xb, cb);                     // step 3
-        interleave_region<MT + NT, 0, 0, MT * NT - (MT + NT)>();
+        order_reads();
         fence();
     };
     auto tail = [&](const char* cur) __attribute__((always_inline)) {
@@ -706,7 +743,6 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         mfma_step(xb, cb);
     };
     static_assert(E / 16 == 4, "the skewed schedule is written for four K steps per stage");
-    static_assert(MT * NT >= MT + NT + 8, "each region's memory instructions need an MFMA each");
 
     // the main loop, in two versions: with |x|^2 (first generator tile) or
     // without (the other tiles; their |x|^2 would be the same)
@@ -1016,6 +1052,11 @@ static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStr
 #ifndef PAMM_COMPRESS_GEMM
 #define PAMM_COMPRESS_GEMM 4, 4, 2, 2
 #endif
+// the same with 128-row blocks (2 x 2 waves of 64 rows x 128 generators), for
+// inputs whose 256-row blocks leave compute units idle
+#ifndef PAMM_COMPRESS_GEMM_HALF
+#define PAMM_COMPRESS_GEMM_HALF 2, 4, 2, 2
+#endif
 #ifndef PAMM_COMPRESS_USE_GEMM
 #define PAMM_COMPRESS_USE_GEMM 1
 #endif
@@ -1023,8 +1064,8 @@ static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStr
 // The GEMM-shaped kernel addresses X with 32-bit offsets from a uniform
 // base: every row offset, plus one stage, must stay below 4 GiB.  With one
 // workgroup per compute unit it also needs at least as many (row block,
-// generator tile) pairs as compute units; with fewer, the 128-row kernel,
-// which runs twice as many workgroups, finishes first.
+// generator tile) pairs as compute units: the 256-row blocks where they fill
+// the device, else 128-row blocks where those do, else the 128-row kernel.
 template <int MT, int NWR>
 static bool gemm_pays(const CompressArgs& a, int ntiles) {
     constexpr int BM = 32 * MT * NWR;
@@ -1043,12 +1084,14 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
         case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
         default:
             if constexpr (DT == DT_BF16) {
-                if (PAMM_COMPRESS_USE_GEMM && a.cn2 && gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles)) {
+                const bool full = gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles);
+                if (PAMM_COMPRESS_USE_GEMM && a.cn2 && (full || gemm_pays_cfg<PAMM_COMPRESS_GEMM_HALF>(a, ntiles))) {
                     const unsigned pblocks = (unsigned)std::min<int64_t>(a.k, 4096);
                     hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
                     const hipError_t e = hipGetLastError();
                     if (e != hipSuccess) return e;
-                    return launch_compress_gemm<PAMM_COMPRESS_GEMM>(a, ntiles, st);
+                    return full ? launch_compress_gemm<PAMM_COMPRESS_GEMM>(a, ntiles, st)
+                                : launch_compress_gemm<PAMM_COMPRESS_GEMM_HALF>(a, ntiles, st);
                 }
             }
             return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);

@@ -158,6 +158,11 @@ GEMM_CASES = [
     (65536, 64, 64, 256, 0.0),      # a single stage (and one padding position)
     (32768, 256, 256, 512, 0.0),    # two full tiles
     (65536, 120, 144, 256, 0.1),    # strided view: ldx > d
+    # 128-row blocks (the 256-row blocks would leave compute units idle)
+    (32845, 136, 136, 256, 0.05),   # ragged n; tail stage; odd stage count
+    (20000, 200, 200, 300, 0.1),    # two tiles, the last one 44 generators
+    (32768, 128, 128, 256, 0.0),    # no tail, even stage count
+    (32768, 120, 144, 256, 0.1),    # strided view
 ]
 
 
@@ -226,11 +231,12 @@ def test_duplicate_generators_and_zero_and_nan_rows():
         check_wgrad(to_host(out["C"]), f_g, a_g, dY, to_host(out["dW"]))
 
 
-def test_gemm_tiles_degenerate_rows():
-    # the same degenerate cases on the GEMM-shaped kernel (bf16, 256 generators,
-    # 256 row blocks): duplicate and collinear generators, a zero generator, a
+@pytest.mark.parametrize("n", [65536, 32768])   # 256- and 128-row blocks
+def test_gemm_tiles_degenerate_rows(n):
+    # the same degenerate cases on the GEMM-shaped kernel (bf16, 256
+    # generators): duplicate and collinear generators, a zero generator, a
     # zero row, a NaN row
-    n, d, k = 65536, 128, 256
+    d, k = 128, 256
     X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 33, "bf16")).copy()
     X32[40] = X32[7]
     X32[41] = -4 * X32[7]
@@ -261,10 +267,11 @@ def test_gemm_tiles_degenerate_rows():
         check_compress(X, g, eps, to_host(C), f_g, a_g)
 
 
-def test_gemm_tiles_degenerate_rows_plain_generators():
+@pytest.mark.parametrize("n", [65536, 32768])
+def test_gemm_tiles_degenerate_rows_plain_generators(n):
     # the same rows with every generator of finite, positive norm (no zero
     # generator, no padding): the epilogue's shorter scan
-    n, d, k = 65536, 128, 256
+    d, k = 128, 256
     X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 35, "bf16")).copy()
     X32[40] = X32[7]
     X32[41] = -4 * X32[7]
