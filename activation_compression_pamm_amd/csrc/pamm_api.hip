@@ -87,24 +87,27 @@ int pamm_sample_generators(int64_t n, int64_t k, uint64_t seed, int32_t* gen_idx
 
 // Workspace of pamm_compress, 256-byte aligned parts:
 //   k > 256:                per-tile winners [ntiles x n] and |x|^2 [n]
-//   bf16 with k > 128:      |c_j|^2 [k] (the 256-generator GEMM-shaped path)
+//   bf16 with k > 64:       |c_j|^2 [k] (the GEMM-shaped paths)
 namespace {
 struct CompressLayout {
     size_t off_partial, off_xn2, off_cn2, total;
+    bool has_partial, has_cn2;
 };
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 CompressLayout compress_layout(int64_t n, int64_t k, int dtype) {
-    CompressLayout L{0, 0, 0, 0};
+    CompressLayout L{0, 0, 0, 0, false, false};
     if (n <= 0) return L;
     size_t off = 0;
     if (k > pamm::kMaxTileGens) {
         const int64_t ntiles = (k + pamm::kMaxTileGens - 1) / pamm::kMaxTileGens;
+        L.has_partial = true;
         L.off_partial = off;
         off += up256(sizeof(pamm::PartialBest) * (size_t)(ntiles * n));
         L.off_xn2 = off;
         off += up256(sizeof(float) * (size_t)n);
     }
-    if (dtype == PAMM_BF16 && k > pamm::kMaxTileGens / 2) {
+    if (dtype == PAMM_BF16 && k > pamm::kMaxTileGens / 4) {
+        L.has_cn2 = true;
         L.off_cn2 = off;
         off += up256(sizeof(float) * (size_t)k);
     }
@@ -150,11 +153,11 @@ int pamm_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int dtype, c
     a.num_cus = num_cus();
     const CompressLayout L = compress_layout(n, k, dtype);
     char* w = reinterpret_cast<char*>(ws);
-    if (k > pamm::kMaxTileGens) {
+    if (L.has_partial) {
         a.partial = reinterpret_cast<pamm::PartialBest*>(w + L.off_partial);
         a.xn2 = reinterpret_cast<float*>(w + L.off_xn2);
     }
-    if (dtype == PAMM_BF16 && k > pamm::kMaxTileGens / 2) a.cn2 = reinterpret_cast<float*>(w + L.off_cn2);
+    if (L.has_cn2) a.cn2 = reinterpret_cast<float*>(w + L.off_cn2);
     const hipError_t e = pamm::run_compress(a, dtype, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? PAMM_OK : PAMM_ERR_HIP;
 }

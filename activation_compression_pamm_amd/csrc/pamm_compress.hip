@@ -508,7 +508,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     constexpr int BM = WM * NWR, BN = WN * NWC;
     constexpr int XPT = BM * 8 / NTH;       // 16-byte X chunks per lane per stage
     constexpr int CPT = BN * 8 / NTH;
-    static_assert(BN == kMaxTileGens, "one generator tile per workgroup");
+    static_assert(BN <= kMaxTileGens && BN % 64 == 0, "one generator tile per workgroup");
     static_assert((BM * 8) % NTH == 0 && (BN * 8) % NTH == 0, "tile shape");
 
     // two stage buffers, each the X tile then the C tile
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // the staged lines of a lane are handled in parts of four chunks: XP
     // parts of X, then CP parts of C
     constexpr int XP = XPT / 4, CP = CPT / 4, NP = XP + CP;
-    static_assert(XPT % 4 == 0 && CPT % 4 == 0 && NP >= 3 && NP <= 4, "the stash is split in three or four parts");
+    static_assert(XPT % 4 == 0 && CPT % 4 == 0 && NP >= 2 && NP <= 4, "the stash is split in two to four parts");
     v4u32 xr[XPT], cr[CPT];
     // per-lane partial |x|^2 of the rows this lane fetches (summed by the
     // workgroups of the first generator tile only; |c|^2 comes from the
@@ -1057,6 +1057,10 @@ static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStr
 #ifndef PAMM_COMPRESS_GEMM_HALF
 #define PAMM_COMPRESS_GEMM_HALF 2, 4, 2, 2
 #endif
+// bf16 tiles of 128 generators: 128-row blocks, 2 x 2 waves of 64 x 64
+#ifndef PAMM_COMPRESS_GEMM128
+#define PAMM_COMPRESS_GEMM128 2, 2, 2, 2
+#endif
 #ifndef PAMM_COMPRESS_USE_GEMM
 #define PAMM_COMPRESS_USE_GEMM 1
 #endif
@@ -1081,7 +1085,17 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
         case 16: return launch_compress_rs<DT, PAMM_COMPRESS_RS16>(a, ntiles, st);
         case 32: return launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
         case 64: return launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
-        case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
+        case 128:
+            if constexpr (DT == DT_BF16) {
+                if (PAMM_COMPRESS_USE_GEMM && a.cn2 && gemm_pays_cfg<PAMM_COMPRESS_GEMM128>(a, ntiles)) {
+                    const unsigned pblocks = (unsigned)std::min<int64_t>(a.k, 4096);
+                    hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
+                    const hipError_t e = hipGetLastError();
+                    if (e != hipSuccess) return e;
+                    return launch_compress_gemm<PAMM_COMPRESS_GEMM128>(a, ntiles, st);
+                }
+            }
+            return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
         default:
             if constexpr (DT == DT_BF16) {
                 const bool full = gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles);

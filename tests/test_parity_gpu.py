@@ -149,8 +149,8 @@ def test_k_equals_n_gives_exact_product(dtype):
     assert e <= (1e-4 if dtype == "bf16" else 1e-5), e
 
 
-# bf16 with 256-generator tiles and at least one (row block, tile) pair per
-# compute unit: the GEMM-shaped compress kernel.  Ragged rows, a tail stage,
+# bf16 with 128- or 256-generator tiles and at least one (row block, tile)
+# pair per compute unit: the GEMM-shaped compress kernel.  Ragged rows, a tail stage,
 # a padding stage position, a partial last tile and a strided view.
 GEMM_CASES = [
     (65573, 136, 136, 256, 0.05),   # ragged n; tail stage of 8; odd stage count
@@ -163,6 +163,10 @@ GEMM_CASES = [
     (20000, 200, 200, 300, 0.1),    # two tiles, the last one 44 generators
     (32768, 128, 128, 256, 0.0),    # no tail, even stage count
     (32768, 120, 144, 256, 0.1),    # strided view
+    # 128-generator tiles (64 < k <= 128), 128-row blocks
+    (32868, 136, 136, 128, 0.05),   # ragged n; tail stage; odd stage count
+    (32768, 128, 128, 100, 0.1),    # a partial tile of 100 generators; no tail
+    (32768, 120, 144, 96, 0.0),     # strided view
 ]
 
 
