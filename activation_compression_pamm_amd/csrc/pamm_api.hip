@@ -87,7 +87,7 @@ int pamm_sample_generators(int64_t n, int64_t k, uint64_t seed, int32_t* gen_idx
 
 // Workspace of pamm_compress, 256-byte aligned parts:
 //   k > 256:                per-tile winners [ntiles x n] and |x|^2 [n]
-//   bf16 with k > 64:       |c_j|^2 [k] (the GEMM-shaped paths)
+//   bf16 with k > 128:      |c_j|^2 [k] (the GEMM-shaped path)
 namespace {
 struct CompressLayout {
     size_t off_partial, off_xn2, off_cn2, total;
@@ -106,7 +106,7 @@ CompressLayout compress_layout(int64_t n, int64_t k, int dtype) {
         L.off_xn2 = off;
         off += up256(sizeof(float) * (size_t)n);
     }
-    if (dtype == PAMM_BF16 && k > pamm::kMaxTileGens / 4) {
+    if (dtype == PAMM_BF16 && k > pamm::kMaxTileGens / 2) {
         L.has_cn2 = true;
         L.off_cn2 = off;
         off += up256(sizeof(float) * (size_t)k);

@@ -597,7 +597,10 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         if (part < XP) {
             const char* bx = X + m0 * a.ldx_bytes + (int64_t)st * RB;
 #pragma unroll
-            for (int i = 4 * part; i < 4 * part + 4; ++i) xr[i] = *reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16));
+            // non-temporal: the X lines need not stay in the memory-side cache
+            // (other generator tiles of the row block re-read them from L2)
+            for (int i = 4 * part; i < 4 * part + 4; ++i)
+                xr[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16)));
         } else {
             const char* bc = X + (int64_t)st * RB;
 #pragma unroll
@@ -1057,10 +1060,6 @@ static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStr
 #ifndef PAMM_COMPRESS_GEMM_HALF
 #define PAMM_COMPRESS_GEMM_HALF 2, 4, 2, 2
 #endif
-// bf16 tiles of 128 generators: 128-row blocks, 2 x 2 waves of 64 x 64
-#ifndef PAMM_COMPRESS_GEMM128
-#define PAMM_COMPRESS_GEMM128 2, 2, 2, 2
-#endif
 #ifndef PAMM_COMPRESS_USE_GEMM
 #define PAMM_COMPRESS_USE_GEMM 1
 #endif
@@ -1085,17 +1084,7 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
         case 16: return launch_compress_rs<DT, PAMM_COMPRESS_RS16>(a, ntiles, st);
         case 32: return launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
         case 64: return launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
-        case 128:
-            if constexpr (DT == DT_BF16) {
-                if (PAMM_COMPRESS_USE_GEMM && a.cn2 && gemm_pays_cfg<PAMM_COMPRESS_GEMM128>(a, ntiles)) {
-                    const unsigned pblocks = (unsigned)std::min<int64_t>(a.k, 4096);
-                    hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
-                    const hipError_t e = hipGetLastError();
-                    if (e != hipSuccess) return e;
-                    return launch_compress_gemm<PAMM_COMPRESS_GEMM128>(a, ntiles, st);
-                }
-            }
-            return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
+        case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
         default:
             if constexpr (DT == DT_BF16) {
                 const bool full = gemm_pays_cfg<PAMM_COMPRESS_GEMM>(a, ntiles);

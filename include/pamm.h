@@ -81,8 +81,8 @@ const char *pamm_status_string(int status);
 int pamm_sample_generators(int64_t n, int64_t k, uint64_t seed, int32_t *gen_idx_host);
 
 /* Bytes of workspace pamm_compress needs: 0 for fp32 with k <= 256 and for
- * bf16 with k <= 64; otherwise per-tile winners and |x|^2 (k > 256) and
- * the generator norms |c_j|^2 (bf16, k > 64). */
+ * bf16 with k <= 128; otherwise per-tile winners and |x|^2 (k > 256) and
+ * the generator norms |c_j|^2 (bf16, k > 128). */
 size_t pamm_compress_workspace_size(int64_t n, int64_t d, int64_t k, int dtype);
 
 /*
@@ -108,9 +108,9 @@ size_t pamm_compress_workspace_size(int64_t n, int64_t d, int64_t k, int dtype);
  * the stored values; the decision is taken in fp32.  The result is bitwise
  * deterministic.  |c_j|^2 is the same accumulation as a dot product, so a row
  * equal to a power-of-two multiple s of a generator gets alpha = s exactly,
- * with one exception: bf16 with k > 64 on inputs that fill the device (at
- * least one (128-row block, generator tile) pair per compute unit) runs a
- * GEMM-shaped kernel that sums |c_j|^2 in fp32 in another order, so there
+ * with one exception: bf16 with k > 128 on inputs that fill the device (at
+ * least one (128-row block, 256-generator tile) pair per compute unit) runs
+ * a GEMM-shaped kernel that sums |c_j|^2 in fp32 in another order, so there
  * such an alpha is s to a few fp32 ulps (its bf16 reconstruction alpha*c
  * still equals the row).
  */

@@ -163,7 +163,7 @@ GEMM_CASES = [
     (20000, 200, 200, 300, 0.1),    # two tiles, the last one 44 generators
     (32768, 128, 128, 256, 0.0),    # no tail, even stage count
     (32768, 120, 144, 256, 0.1),    # strided view
-    # 128-generator tiles (64 < k <= 128), 128-row blocks
+    # 64 < k <= 128 at the same sizes (the 128-row kernel)
     (32868, 136, 136, 128, 0.05),   # ragged n; tail stage; odd stage count
     (32768, 128, 128, 100, 0.1),    # a partial tile of 100 generators; no tail
     (32768, 120, 144, 96, 0.0),     # strided view
