@@ -233,31 +233,36 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
         }
         __syncthreads();
     } else {
-        // the first HB histogram entries of this thread are loaded before
-        // the bins are cleared, so their latency overlaps the clearing
-        constexpr int HB = 8;
-        const int64_t total = a.nb * k;
-        const int64_t pre_end = b * k;  // entries of blocks before this one
-        int hv[HB];
-#pragma unroll
-        for (int u = 0; u < HB; ++u) {
-            const int64_t e = t + 256 * u;
-            hv[u] = e < total ? a.hist[e] : 0;
-        }
+        // column sums of the histogram: R threads share a generator column
+        // (R = 256 / k for k < 256, else 1), thread t summing the blocks
+        // t / k, t / k + R, ... with HB loads issued before any add; the R
+        // partial sums meet in LDS integer atomics (exact, in any order)
+        constexpr int HB = 16;
+        const int R = k >= 256 ? 1 : 256 / k;
+        const int r = k >= 256 ? 0 : t / k;
         for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
         for (int j = t; j < k; j += 256) { s_tot[j] = 0; s_base[j] = 0; }
         __syncthreads();
-        auto add = [&](int64_t e, int h) {
-            if (h) {
-                const int j = (int)(e % k);
-                atomicAdd(&s_tot[j], h);
-                if (e < pre_end) atomicAdd(&s_base[j], h);
-            }
-        };
+        if (r < R) {
+            for (int j = k >= 256 ? t : t % k; j < k; j += 256) {
+                int tot = 0, pre = 0;
+                for (int64_t b0 = r; b0 < a.nb; b0 += (int64_t)R * HB) {
+                    int hv[HB];
 #pragma unroll
-        for (int u = 0; u < HB; ++u) add(t + 256 * u, hv[u]);
-#pragma unroll 8
-        for (int64_t e = t + 256 * HB; e < total; e += 256) add(e, a.hist[e]);
+                    for (int u = 0; u < HB; ++u) {
+                        const int64_t bb = b0 + (int64_t)u * R;
+                        hv[u] = bb < a.nb ? a.hist[bb * k + j] : 0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < HB; ++u) {
+                        tot += hv[u];
+                        if (b0 + (int64_t)u * R < b) pre += hv[u];
+                    }
+                }
+                if (tot) atomicAdd(&s_tot[j], tot);
+                if (pre) atomicAdd(&s_base[j], pre);
+            }
+        }
         __syncthreads();
     }
 
