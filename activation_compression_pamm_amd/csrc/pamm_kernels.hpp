@@ -11,8 +11,13 @@ namespace pamm {
 // Generators handled by one compress workgroup; larger k is split into tiles
 // whose winners are merged.
 constexpr int kMaxTileGens = 256;
-// Rows of one chunk of a generator's row list in the wgrad scatter-reduce.
-constexpr int kChunkRows = 256;
+// Rows of one chunk of a generator's row list in the wgrad scatter-reduce:
+// kMaxChunkRows, halved down to kMinChunkRows while the upper bound on
+// (chunk, 64-column slab) items stays below kFillItems (the waves a full
+// device holds), so that small problems still spread over the device.
+constexpr int kMaxChunkRows = 256;
+constexpr int kMinChunkRows = 64;
+constexpr int64_t kFillItems = 8192;
 // Rows handled by one block of the wgrad counting sort.
 constexpr int kSortBlockRows = 1024;
 // Above this many histogram entries (sort blocks x generators) the histogram
@@ -49,6 +54,7 @@ hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st);
 // Workspace carve-up of pamm_wgrad (all offsets 256-byte aligned).
 struct WgradLayout {
     int64_t nb;         // sort blocks
+    int chunk_rows;     // rows per chunk (a generator's last chunk may hold fewer)
     int64_t max_chunks; // upper bound on row chunks
     size_t off_hist, off_tot, off_nchunks, off_chunk_gen, off_chunk_begin, off_chunk_count;
     size_t off_perm, off_palpha, off_AT, off_BT;

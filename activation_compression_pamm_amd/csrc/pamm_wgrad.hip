@@ -17,7 +17,7 @@
 //                      prefixes, ranks its rows with wave ballots and writes
 //                      (row, alpha) in generator order; block 0 also cuts
 //                      each generator's rows into chunks of at most
-//                      kChunkRows rows.
+//                      chunk_rows rows (chosen with the workspace layout).
 //   3. scatter_reduce  gathers the product's A operand (each chunk's
 //                      generator row of C, in MFMA fragment order), then
 //                      one wave per (chunk, 128-byte column slab): sums
@@ -187,6 +187,7 @@ struct SortScatterArgs {
     int64_t n;
     int k;
     int nbits;
+    int chunk_rows;
     int64_t nb;
     const int32_t* hist;   // [nb][k] per-block counts, or (PREFIXED) exclusive prefixes along the blocks
     const int32_t* totals; // [k] segment sizes (PREFIXED only)
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     // block 0 cuts every generator's rows into chunks (before s_tot becomes starts)
     if (b == 0) {
         int* s_nch = s_w;  // reuse: per-generator chunk count -> first chunk
-        for (int j = t; j < k; j += 256) s_nch[j] = (s_tot[j] + kChunkRows - 1) / kChunkRows;
+        for (int j = t; j < k; j += 256) s_nch[j] = (s_tot[j] + a.chunk_rows - 1) / a.chunk_rows;
         __syncthreads();
         const int total_chunks = block_exclusive_scan(s_nch, k, s_tmp);
         if (t == 0) *a.nchunks = total_chunks;
@@ -283,10 +284,10 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
             const int start = s_tot[j];
             const int size = (j + 1 < k ? s_tot[j + 1] : total_rows) - start;
             const int c0 = s_nch[j];
-            for (int c = 0; c * kChunkRows < size; ++c) {
+            for (int c = 0; c * a.chunk_rows < size; ++c) {
                 a.chunk_gen[c0 + c] = j;
-                a.chunk_begin[c0 + c] = start + c * kChunkRows;
-                a.chunk_count[c0 + c] = min(kChunkRows, size - c * kChunkRows);
+                a.chunk_begin[c0 + c] = start + c * a.chunk_rows;
+                a.chunk_count[c0 + c] = min(a.chunk_rows, size - c * a.chunk_rows);
             }
         }
         __syncthreads();
@@ -730,7 +731,13 @@ WgradLayout wgrad_layout(int64_t n, int64_t k, int64_t d, int64_t d_out) {
     WgradLayout L;
     L.nb = (n + kSortBlockRows - 1) / kSortBlockRows;
     if (L.nb < 1) L.nb = 1;
-    L.max_chunks = (n + kChunkRows - 1) / kChunkRows + k;
+    // chunk length: halved while even the most chunks it allows would give
+    // fewer (chunk, 64-column slab) items than a full device has waves
+    const int64_t slabs = (d_out + 63) / 64;
+    int cr = kMaxChunkRows;
+    while (cr > kMinChunkRows && ((n + cr - 1) / cr + k) * slabs < kFillItems) cr /= 2;
+    L.chunk_rows = cr;
+    L.max_chunks = (n + cr - 1) / cr + k;
     size_t off = 0;
     L.off_hist = off; off = align256(off + sizeof(int32_t) * (size_t)(L.nb * (k > 0 ? k : 1)));
     L.off_tot = off; off = align256(off + sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
@@ -790,6 +797,7 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         int nbits = 0;
         while ((1 << nbits) < k) ++nbits;
         s.nbits = nbits;
+        s.chunk_rows = L.chunk_rows;
         s.nb = L.nb; s.hist = hist; s.totals = tot; s.nchunks = nchunks;
         s.chunk_gen = cgen; s.chunk_begin = cbeg; s.chunk_count = ccnt; s.perm = perm; s.palpha = palpha;
         const size_t lds = sizeof(int) * (6 * (size_t)k + 256);

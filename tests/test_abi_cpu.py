@@ -71,6 +71,11 @@ def test_workspace_sizes(lib):
     # chunk partial rows (n/256 + k) x d_out fp32 dominate
     assert w >= (32768 // 256 + 64) * 12288 * 4
     assert w % 256 == 0
+    # a small problem (n = 8192, 16 generators, 36 column slabs) is cut into
+    # 64-row chunks so that its items fill the device: room for n/64 + k rows
+    w = lib.pamm_wgrad_workspace_size(8192, 16, 768, 2304, 1)
+    assert w >= (8192 // 64 + 16) * 2304 * 4
+    assert w < (8192 // 32 + 16) * 2304 * 4
 
 
 def call_compress(lib, X=FAKE, n=64, d=32, ldx=32, dt=1, gen=FAKE, k=4, eps=0.1, C=FAKE, f=FAKE, a=FAKE,
