@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
     extern __shared__ int s_dyn[];
     const int k = a.k;
     int* s_tot = s_dyn;          // [k]   segment sizes, then segment starts
-    int* s_base = s_dyn + k;     // [k]   rows of this generator in earlier blocks, then start of this block
+    int* s_base = s_dyn + k;     // [k]   rows of this generator in earlier blocks
     int* s_w = s_dyn + 2 * k;    // [4][k] per-wave counts, then per-wave running positions
     int* s_tmp = s_dyn + 6 * k;  // [256] scan scratch
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -294,9 +294,6 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
         for (int j = t; j < 4 * k; j += 256) s_w[j] = 0;
         __syncthreads();
     }
-    for (int j = t; j < k; j += 256) s_base[j] += s_tot[j];  // first position of this block's rows
-    __syncthreads();
-
     // per-wave counts over the wave's 256 rows
     bool ok[4];
 #pragma unroll
@@ -307,9 +304,10 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortScatterArgs a) {
         if (ok[sub]) atomicAdd(&s_w[wave * k + fi], 1);
     }
     __syncthreads();
-    // running position of each wave := block start + counts of earlier waves
+    // running position of each wave := segment start + rows of earlier
+    // blocks + counts of earlier waves
     for (int j = t; j < k; j += 256) {
-        int run = s_base[j];
+        int run = s_tot[j] + s_base[j];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const int c = s_w[w * k + j];
