@@ -76,6 +76,9 @@ def test_workspace_sizes(lib):
     w = lib.pamm_wgrad_workspace_size(8192, 16, 768, 2304, 1)
     assert w >= (8192 // 64 + 16) * 2304 * 4
     assert w < (8192 // 32 + 16) * 2304 * 4
+    # in between (n = 20000, 64 slabs): 128-row chunks
+    w = lib.pamm_wgrad_workspace_size(20000, 16, 32, 4096, 1)
+    assert (20000 // 128 + 16) * 4096 * 4 <= w < (20000 // 64 + 16) * 4096 * 4
 
 
 def call_compress(lib, X=FAKE, n=64, d=32, ldx=32, dt=1, gen=FAKE, k=4, eps=0.1, C=FAKE, f=FAKE, a=FAKE,

@@ -98,6 +98,7 @@ def test_long_segments_split_into_chunks():
     (65537, 32, 64, 40),     # a last sort block of one row
     (6000, 64, 96, 4096),    # the largest k (LDS beyond 64 KB in the sort)
     (300000, 16, 16, 16),    # 293 sort blocks summing a small histogram
+    (20000, 32, 4096, 16),   # 128-row chunks (the layout halves 256 once)
 ])
 def test_sort_block_edges_and_largest_k(n, d, dout, k):
     X = synth.clustered_activations(n, d, 64, seed=n + k, dtype="bf16")
