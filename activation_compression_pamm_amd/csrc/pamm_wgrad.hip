@@ -45,6 +45,11 @@
 #ifndef PAMM_SR_U
 #define PAMM_SR_U 8
 #endif
+// with full-length chunks, generators averaging at most this many rows (n / k,
+// as if every row were kept) get paired reduction items: two chunks per item
+#ifndef PAMM_SR_PAIR_ROWS
+#define PAMM_SR_PAIR_ROWS 128
+#endif
 // dW tile of one wave: 32*TM rows x 32*TN columns (32*TN_WIDE columns from
 // kWideProductK generators on)
 #ifndef PAMM_GEMM_TM
@@ -390,14 +395,20 @@ __device__ __forceinline__ void write_a_slot(const ScatterArgs& a, int64_t slot,
 // Items: first the A slots, then one per (chunk, column slab).  For the
 // latter LPR lanes cover one row piece of 16*LPR bytes (whole 128-byte
 // lines), 64/LPR row groups walk the chunk's rows, U rows per group in
-// flight.
-template <int DT, int LPR, int U>
+// flight.  PAIR (for short chunks): an item is a pair of consecutive chunks
+// at one slab, each half of the wave's row groups walking one of them, so
+// that an item still gathers up to 64 rows at once.
+template <int DT, int LPR, int U, bool PAIR>
 __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
     constexpr int PE = Elem<DT>::per16;   // elements per lane
     constexpr int SC = LPR * PE;          // columns per slab
     constexpr int RG = 64 / LPR;          // row groups per wave
+    constexpr int HALVES = PAIR ? 2 : 1;  // chunks per item
+    constexpr int RGH = RG / HALVES;      // row groups per chunk
+    constexpr int BR = RGH * U;           // rows of a chunk per batch
     const int lane = threadIdx.x & 63;
     const int g = lane / LPR, lq = lane % LPR;
+    const int h = g / RGH, gh = g % RGH;  // chunk of the item, row group in it
     // chunks up to the next multiple of 16 are written too (as zeros), so
     // the product's last contraction step holds no stale workspace
     const int nch = *a.nchunks;
@@ -409,23 +420,24 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
 
     // one batch is the 64 rows the wave's row groups take together
     static_assert(RG * U == 64, "a batch is 64 rows");
-    const int64_t nitems = (int64_t)ks_used * 16 * a.nslab;
+    static_assert(!PAIR || (RG == 8 && PE >= 4), "paired items: 8 row groups, 4 or 8 columns per lane");
+    const int64_t nitems = (int64_t)ks_used * (16 / HALVES) * a.nslab;
     auto meta = [&](int64_t it, int& bg, int& cn) {
-        const int64_t c = it / a.nslab;
+        const int64_t c = it / a.nslab * HALVES + h;
         bg = c < nch ? a.chunk_begin[c] : 0;
         cn = c < nch ? a.chunk_count[c] : 0;
     };
     auto row_ids = [&](int bg, int cn, int t0, int* ii) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tt = t0 + RG * u;
+            const int tt = t0 + RGH * u;
             ii[u] = tt < cn ? a.perm[bg + tt] : -1;
         }
     };
     auto row_alphas = [&](int bg, int cn, int t0, float* aa) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tt = t0 + RG * u;
+            const int tt = t0 + RGH * u;
             aa[u] = tt < cn ? a.palpha[bg + tt] : 0.f;
         }
     };
@@ -461,96 +473,116 @@ __global__ __launch_bounds__(256) void scatter_reduce_kernel(ScatterArgs a) {
     if (wave < nitems) {
         meta(wave, b0, c0);
         int ii[U];
-        row_ids(b0, c0, g, ii);
-        row_alphas(b0, c0, g, aa);
+        row_ids(b0, c0, gh, ii);
+        row_alphas(b0, c0, gh, aa);
         fetch(wave, ii, vv);
     }
     if (wave + wstride < nitems) {
         meta(wave + wstride, b1, c1);
-        row_ids(b1, c1, g, jj);
+        row_ids(b1, c1, gh, jj);
     }
     if (wave + 2 * wstride < nitems) meta(wave + 2 * wstride, b2, c2);
     for (int64_t item = wave; item < nitems; item += wstride) {
-        const int64_t ch = item / a.nslab;
+        const int64_t ch = item / a.nslab * HALVES + h;
         const int64_t col = (item % a.nslab) * SC + lq * PE;
         float acc[PE];
 #pragma unroll
         for (int e = 0; e < PE; ++e) acc[e] = 0.f;
         accumulate(vv, aa, acc);  // first batch, fetched ahead
-        const int nbatch = (c0 + 63) >> 6;
+        const int nbatch = (c0 + BR - 1) / BR;
         for (int bt = 1; bt < nbatch; ++bt) {
             int ii[U];
-            row_ids(b0, c0, g + 64 * bt, ii);
-            row_alphas(b0, c0, g + 64 * bt, aa);
+            row_ids(b0, c0, gh + BR * bt, ii);
+            row_alphas(b0, c0, gh + BR * bt, aa);
             fetch(item, ii, vv);
             accumulate(vv, aa, acc);
         }
         const int64_t n1 = item + wstride, n2 = n1 + wstride, n3 = n2 + wstride;
         if (n1 < nitems) {
             fetch(n1, jj, vv);
-            row_alphas(b1, c1, g, aa);
+            row_alphas(b1, c1, gh, aa);
         }
-        if (n2 < nitems) row_ids(b2, c2, g, jj);
+        if (n2 < nitems) row_ids(b2, c2, gh, jj);
         int b3 = 0, c3 = 0;
         if (n3 < nitems) meta(n3, b3, c3);
         b0 = b1; c0 = c1;
         b1 = b2; c1 = c2;
         b2 = b3; c2 = c3;
-        // fixed-order combine of the row groups; lane g of each group then
-        // stores column g of its PE columns.  With as many groups as columns
-        // (bf16) the combine is a reduce-scatter: at each step a lane keeps
-        // half of its columns and adds the partner's sums for them (7
-        // exchanges instead of 24); otherwise every lane sums all columns.
-        float v;
-        if constexpr (PE == 8 && RG == 8) {
-            const bool h4 = g & 4, h2 = g & 2, h1 = g & 1;
-            float r4[4], r2[2];
+        // lane stores of column n of this item's chunk straight into the B
+        // fragments (B[n][kk] = P[kk][n]): bf16 lane l, piece 0 holds
+        // B[32nb + l%32][16ks + 8(l/32) + 0..7], split into a hi and a lo
+        // bf16 term (lo blocks after all hi blocks); fp32 lane l, piece h
+        // holds B[32nb + l%32][16ks + 8h + 4(l/32) + 0..3]
+        auto store = [&](int64_t n, float v) __attribute__((always_inline)) {
+            if (n >= a.ncols) return;
+            const int64_t nb = n >> 5, ks = ch >> 4;
+            const int nl = (int)(n & 31), c16 = (int)(ch & 15);
+            if constexpr (DT == DT_BF16) {
+                const int64_t idx = ((nb * a.ks_cap + ks) * 64 + nl + 32 * (c16 >> 3)) * 8 + (c16 & 7);
+                const uint32_t hi = f32_to_bf16(v);
+                const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
+                uint16_t* bf = reinterpret_cast<uint16_t*>(a.BF);
+                bf[idx] = (uint16_t)hi;
+                bf[idx + (a.ncols >> 5) * a.ks_cap * 64 * 8] = (uint16_t)lo;
+            } else {
+                const int64_t idx =
+                    (((nb * a.ks_cap + ks) * 2 + (c16 >> 3)) * 64 + nl + 32 * ((c16 >> 2) & 1)) * 4 + (c16 & 3);
+                reinterpret_cast<float*>(a.BF)[idx] = v;
+            }
+        };
+        // fixed-order combine of the row groups of a chunk.  With as many
+        // groups as columns (bf16) the combine is a reduce-scatter: at each
+        // step a lane keeps half of its columns and adds the partner's sums
+        // for them (7 exchanges instead of 24), and lane g of each group
+        // stores column g; otherwise every lane sums all columns.  Paired
+        // items reduce-scatter over the 4 groups of each half (lanes 8 and
+        // 16 apart), leaving PE/4 columns per lane.
+        if constexpr (PAIR) {
+            constexpr int HALF = PE / 2, Q = PE / 4;
+            const bool b1 = gh & 2, b0 = gh & 1;
+            float r[HALF], q[Q];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float keep = h4 ? acc[4 + j] : acc[j];
-                r4[j] = keep + shfl_xor(h4 ? acc[j] : acc[4 + j], 32);
+            for (int j = 0; j < HALF; ++j) {
+                const float keep = b1 ? acc[HALF + j] : acc[j];
+                r[j] = keep + shfl_xor(b1 ? acc[j] : acc[HALF + j], 16);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float keep = h2 ? r4[2 + j] : r4[j];
-                r2[j] = keep + shfl_xor(h2 ? r4[j] : r4[2 + j], 16);
+            for (int j = 0; j < Q; ++j) {
+                const float keep = b0 ? r[Q + j] : r[j];
+                q[j] = keep + shfl_xor(b0 ? r[j] : r[Q + j], 8);
             }
-            // lanes l and l^8 share a row of 16 lanes: a DPP rotation by 8
-            const float send = h1 ? r2[0] : r2[1];
-            const int sx = __builtin_bit_cast(int, send);
-            v = (h1 ? r2[1] : r2[0]) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(sx, sx, 0x128, 0xf, 0xf, false));
+#pragma unroll
+            for (int j = 0; j < Q; ++j) store(col + Q * gh + j, q[j]);
         } else {
+            float v;
+            if constexpr (PE == 8 && RG == 8) {
+                const bool h4 = g & 4, h2 = g & 2, h1 = g & 1;
+                float r4[4], r2[2];
 #pragma unroll
-            for (int m = LPR; m < 64; m <<= 1)
-#pragma unroll
-                for (int e = 0; e < PE; ++e) acc[e] += shfl_xor(acc[e], m);
-            v = acc[0];
-#pragma unroll
-            for (int e = 1; e < PE; ++e) v = g == e ? acc[e] : v;
-        }
-        // lane g stores straight into the B fragments (B[n][kk] =
-        // P[kk][n]): bf16 lane l, piece 0 holds B[32nb + l%32][16ks +
-        // 8(l/32) + 0..7], split into a hi and a lo bf16 term (lo blocks
-        // after all hi blocks); fp32 lane l, piece h holds B[32nb +
-        // l%32][16ks + 8h + 4(l/32) + 0..3]
-        if (g < PE) {
-            const int64_t n = col + g;
-            if (n < a.ncols) {
-                const int64_t nb = n >> 5, ks = ch >> 4;
-                const int nl = (int)(n & 31), c16 = (int)(ch & 15);
-                if constexpr (DT == DT_BF16) {
-                    const int64_t idx = ((nb * a.ks_cap + ks) * 64 + nl + 32 * (c16 >> 3)) * 8 + (c16 & 7);
-                    const uint32_t hi = f32_to_bf16(v);
-                    const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
-                    uint16_t* bf = reinterpret_cast<uint16_t*>(a.BF);
-                    bf[idx] = (uint16_t)hi;
-                    bf[idx + (a.ncols >> 5) * a.ks_cap * 64 * 8] = (uint16_t)lo;
-                } else {
-                    const int64_t idx =
-                        (((nb * a.ks_cap + ks) * 2 + (c16 >> 3)) * 64 + nl + 32 * ((c16 >> 2) & 1)) * 4 + (c16 & 3);
-                    reinterpret_cast<float*>(a.BF)[idx] = v;
+                for (int j = 0; j < 4; ++j) {
+                    const float keep = h4 ? acc[4 + j] : acc[j];
+                    r4[j] = keep + shfl_xor(h4 ? acc[j] : acc[4 + j], 32);
                 }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float keep = h2 ? r4[2 + j] : r4[j];
+                    r2[j] = keep + shfl_xor(h2 ? r4[j] : r4[2 + j], 16);
+                }
+                // lanes l and l^8 share a row of 16 lanes: a DPP rotation by 8
+                const float send = h1 ? r2[0] : r2[1];
+                const int sx = __builtin_bit_cast(int, send);
+                v = (h1 ? r2[1] : r2[0]) +
+                    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(sx, sx, 0x128, 0xf, 0xf, false));
+            } else {
+#pragma unroll
+                for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+                    for (int e = 0; e < PE; ++e) acc[e] += shfl_xor(acc[e], m);
+                v = acc[0];
+#pragma unroll
+                for (int e = 1; e < PE; ++e) v = g == e ? acc[e] : v;
             }
+            if (g < PE) store(col + g, v);
         }
     }
 }
@@ -828,7 +860,12 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
         const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 8;
         if (grid > cap) grid = cap;
         if (grid < 1) grid = 1;
-        hipLaunchKernelGGL((scatter_reduce_kernel<DT, PAMM_SR_LPR, PAMM_SR_U>), dim3((unsigned)grid), dim3(256), 0, st, r);
+        if (L.chunk_rows == kMaxChunkRows && a.n <= (int64_t)PAMM_SR_PAIR_ROWS * a.k)
+            hipLaunchKernelGGL((scatter_reduce_kernel<DT, PAMM_SR_LPR, PAMM_SR_U, true>), dim3((unsigned)grid), dim3(256),
+                               0, st, r);
+        else
+            hipLaunchKernelGGL((scatter_reduce_kernel<DT, PAMM_SR_LPR, PAMM_SR_U, false>), dim3((unsigned)grid), dim3(256),
+                               0, st, r);
     } else {
         // no generators or no rows: no chunks, dW = 0 (or unchanged when accumulating)
         hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, st, nchunks);

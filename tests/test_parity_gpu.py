@@ -107,6 +107,19 @@ def test_sort_block_edges_and_largest_k(n, d, dout, k):
     full_case(X, dY, g, 0.05, "sort-path")
 
 
+@pytest.mark.parametrize("n,d,dout,k,dtype", [
+    (20000, 64, 1024, 512, "f32"),
+    (30001, 72, 1544, 300, "bf16"),   # ragged rows and output columns
+])
+def test_paired_reduction_items(n, d, dout, k, dtype):
+    # full-length (256-row) chunks with few rows per generator: each
+    # reduction item walks two chunks, one per half of the wave's row groups
+    X = synth.clustered_activations(n, d, k // 2, seed=n + k, dtype=dtype)
+    dY = synth.gradients(n, dout, seed=n + dout, dtype=dtype)
+    g = pamm.sample_generators(n, k, seed=k + 11).numpy()
+    full_case(X, dY, g, 0.1, f"paired-{dtype}")
+
+
 def _random_case(i):
     # shapes, generator counts and thresholds drawn from one seeded stream;
     # row lengths a multiple of 16 bytes (the ABI's leading-dimension rule)
