@@ -25,6 +25,8 @@
 //                      only kept rows, each 128-byte row piece by 8 lanes,
 //                      and writes the chunk's partial row P[chunk, slab]
 //                      (fp32) straight into the product's B operand.
+//                      With few rows per generator a wave item is a pair
+//                      of chunks, one per half of the row groups.
 //                      Fixed summation order, no atomics: deterministic.
 //   4. gen_gemm        dW = sum over chunks of c_gen(chunk) (x) P[chunk],
 //                      i.e. C^T B~ with B~ split into its chunk partials.
