@@ -166,17 +166,47 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _need(where, name, t, shape, dtype):
+    """A caller-supplied tensor must have exactly this shape and dtype and be
+    contiguous: the kernels read and write it as a dense array."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{where}: {name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{where}: {name} must be contiguous")
+
+
+def _check_triple(where, C, f, alpha, n, k, d, dtype):
+    torch = _torch()
+    if C is not None:
+        _need(where, "C", C, (k, d), dtype)
+    if f is not None:
+        _need(where, "f", f, (n,), torch.int32)
+    if alpha is not None:
+        _need(where, "alpha", alpha, (n,), torch.float32)
+
+
+def _check_workspace(where, workspace):
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError(f"{where}: workspace must be contiguous")
+
+
 def compress(X, gen_idx, eps: float, *, C=None, f=None, alpha=None, workspace=None, stream=None):
     """Compress activations X [n x d] (CUDA/HIP tensor, bf16 or fp32).
 
     gen_idx: int32 device tensor of k generator row ids (see sample_generators).
     Returns (C [k x d], f [n] int32, alpha [n] fp32)."""
     torch = _torch()
-    _on_gpu("compress", X=X, C=C, f=f, alpha=alpha, workspace=workspace)
     n, d, ldx = _rows(X, "X")
     dt = _dtype_code(X)
-    gen_idx = gen_idx.to(device=X.device, dtype=torch.int32).contiguous()
+    if gen_idx.dim() != 1:
+        raise ValueError(f"compress: gen_idx must be 1-D, got shape {tuple(gen_idx.shape)}")
     k = gen_idx.numel()
+    _check_triple("compress", C, f, alpha, n, k, d, X.dtype)
+    _check_workspace("compress", workspace)
+    _on_gpu("compress", X=X, C=C, f=f, alpha=alpha, workspace=workspace)
+    gen_idx = gen_idx.to(device=X.device, dtype=torch.int32).contiguous()
     if C is None:
         C = torch.empty((k, d), dtype=X.dtype, device=X.device)
     if f is None:
@@ -198,17 +228,21 @@ def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: 
     transpose_out the result is dW^T [d_out x d], the layout of the weight
     gradient of a layer Y = X W^T."""
     torch = _torch()
-    _on_gpu("wgrad", C=C, f=f, alpha=alpha, dY=dY, dW=dW, workspace=workspace)
-    k, d = C.shape
     n, d_out, lddy = _rows(dY, "dY")
     dt = _dtype_code(dY)
+    if C.dim() != 2:
+        raise ValueError(f"wgrad: C must be 2-D [k x d], got shape {tuple(C.shape)}")
     if C.dtype != dY.dtype:
         raise TypeError("C and dY must share a dtype")
+    k, d = C.shape
+    _check_triple("wgrad", C, f, alpha, n, k, d, dY.dtype)
+    _check_workspace("wgrad", workspace)
     shape = (d_out, d) if transpose_out else (d, d_out)
+    if dW is not None and (tuple(dW.shape) != shape or dW.dtype != torch.float32):
+        raise ValueError(f"dW must be float32 of shape {shape}, got {tuple(dW.shape)} {dW.dtype}")
+    _on_gpu("wgrad", C=C, f=f, alpha=alpha, dY=dY, dW=dW, workspace=workspace)
     if dW is None:
         dW = torch.empty(shape, dtype=torch.float32, device=dY.device)
-    if tuple(dW.shape) != shape or dW.dtype != torch.float32:
-        raise ValueError(f"dW must be float32 of shape {shape}, got {tuple(dW.shape)} {dW.dtype}")
     _, _, lddw = _rows(dW, "dW")
     ws = _workspace(wgrad_workspace_size(n, k, d, d_out, dt), dY.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -222,14 +256,19 @@ def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: 
 def decompress(C, f, alpha, *, out=None, stream=None):
     """Reconstruction X~_i = alpha_i C_f(i) (zero rows where f = -1)."""
     torch = _torch()
-    _on_gpu("decompress", C=C, f=f, alpha=alpha, out=out)
+    if C.dim() != 2:
+        raise ValueError(f"decompress: C must be 2-D [k x d], got shape {tuple(C.shape)}")
     k, d = C.shape
+    if f.dim() != 1:
+        raise ValueError(f"decompress: f must be 1-D, got shape {tuple(f.shape)}")
     n = f.numel()
     dt = _dtype_code(C)
+    _check_triple("decompress", C, f, alpha, n, k, d, C.dtype)
+    if out is not None and (tuple(out.shape) != (n, d) or out.dtype != C.dtype):
+        raise ValueError(f"out must be {C.dtype} of shape {(n, d)}, got {tuple(out.shape)} {out.dtype}")
+    _on_gpu("decompress", C=C, f=f, alpha=alpha, out=out)
     if out is None:
         out = torch.empty((n, d), dtype=C.dtype, device=f.device)
-    if tuple(out.shape) != (n, d) or out.dtype != C.dtype:
-        raise ValueError(f"out must be {C.dtype} of shape {(n, d)}, got {tuple(out.shape)} {out.dtype}")
     _, _, ldxt = _rows(out, "out")
     st = load_library().pamm_decompress(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, dt, _ptr(out), ldxt,
                                         _stream_ptr(stream))

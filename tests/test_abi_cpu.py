@@ -157,3 +157,53 @@ def test_binding_refuses_without_library(monkeypatch):
     monkeypatch.setattr(pamm, "_LIB_PATH", "/nonexistent/libpamm.so")
     with pytest.raises(RuntimeError, match="not built"):
         pamm.load_library()
+
+
+def test_binding_checks_arrays_before_any_launch():
+    # Every caller-supplied array is checked for shape, dtype and contiguity
+    # before the device check and before the library is called: a short f or
+    # alpha would otherwise be read or written past its end by the kernels.
+    torch = pytest.importorskip("torch")
+    n, d, k, dout = 8, 16, 2, 24
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    X = torch.zeros(n, d, dtype=bf)
+    g = torch.zeros(k, dtype=i32)
+    C = torch.zeros(k, d, dtype=bf)
+    f = torch.zeros(n, dtype=i32)
+    a = torch.zeros(n, dtype=f32)
+    dY = torch.zeros(n, dout, dtype=bf)
+    bad = [
+        ("compress", lambda: pamm.compress(X, g, 0.0, f=torch.zeros(n - 1, dtype=i32)), ValueError, "f must have shape"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, alpha=torch.zeros(n + 1, dtype=f32)), ValueError, "alpha must"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, f=torch.zeros(n, dtype=torch.int64)), TypeError, "f must be"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, alpha=torch.zeros(n, dtype=bf)), TypeError, "alpha must be"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, C=torch.zeros(k, d + 1, dtype=bf)), ValueError, "C must have"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, C=torch.zeros(k, d, dtype=f32)), TypeError, "C must be"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, C=torch.zeros(d, k, dtype=bf).t()), ValueError, "contiguous"),
+        ("compress", lambda: pamm.compress(X, g.view(1, k), 0.0), ValueError, "gen_idx must be 1-D"),
+        ("compress", lambda: pamm.compress(X, g, 0.0, f=torch.zeros(2 * n, dtype=i32)[::2]), ValueError, "contiguous"),
+        ("wgrad", lambda: pamm.wgrad(C, f[:-1], a, dY), ValueError, "f must have shape"),
+        ("wgrad", lambda: pamm.wgrad(C, f, a[:-1], dY), ValueError, "alpha must have shape"),
+        ("wgrad", lambda: pamm.wgrad(C, f.to(torch.int64), a, dY), TypeError, "f must be"),
+        ("wgrad", lambda: pamm.wgrad(C, f, a.to(torch.float64), dY), TypeError, "alpha must be"),
+        ("wgrad", lambda: pamm.wgrad(torch.zeros(d, k, dtype=bf).t(), f, a, dY), ValueError, "contiguous"),
+        ("wgrad", lambda: pamm.wgrad(C.view(-1), f, a, dY), ValueError, "C must be 2-D"),
+        ("wgrad", lambda: pamm.wgrad(C.float(), f, a, dY), TypeError, "share a dtype"),
+        ("wgrad", lambda: pamm.wgrad(C, f, a, dY, dW=torch.zeros(d, dout + 1)), ValueError, "dW must be"),
+        ("wgrad", lambda: pamm.wgrad(C, f, a, dY, dW=torch.zeros(d, dout, dtype=torch.float64)), ValueError,
+         "dW must be"),
+        ("decompress", lambda: pamm.decompress(C, f, a[:-1]), ValueError, "alpha must have shape"),
+        ("decompress", lambda: pamm.decompress(C, f.to(torch.int64), a), TypeError, "f must be"),
+        ("decompress", lambda: pamm.decompress(torch.zeros(d, k, dtype=bf).t(), f, a), ValueError, "contiguous"),
+        ("decompress", lambda: pamm.decompress(C, f.view(2, -1), a), ValueError, "f must be 1-D"),
+        ("decompress", lambda: pamm.decompress(C, f, a, out=torch.zeros(n, d, dtype=f32)), ValueError, "out must be"),
+    ]
+    for where, call, exc, msg in bad:
+        with pytest.raises(exc, match=msg):
+            call()
+    # well-formed host arrays pass these checks and stop at the device check
+    for call in (lambda: pamm.compress(X, g, 0.0, C=C, f=f, alpha=a),
+                 lambda: pamm.wgrad(C, f, a, dY),
+                 lambda: pamm.decompress(C, f, a)):
+        with pytest.raises(ValueError, match="must be on the GPU"):
+            call()

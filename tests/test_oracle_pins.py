@@ -311,6 +311,71 @@ def test_reconstruction_associativity():
     assert rel(orc.wgrad(r["C"], r["f"], r["alpha"], dY), x64.T @ orc.to_f64(dY)) < 1e-12
 
 
+# --------------------------------------------------------------------------
+# the reconstruction's rounding to bf16 (reading R9: the fp32 product alpha*c
+# rounded to the storage dtype, nearest-even)
+# --------------------------------------------------------------------------
+
+def _is_nan_bf16(h):
+    h = np.asarray(h, dtype=np.uint16)
+    return ((h & 0x7f80) == 0x7f80) & ((h & 0x007f) != 0)
+
+
+def test_reconstruction_rounding_golden_table():
+    # each golden fp32 value v is reconstructed as v * 1.0 (one generator equal
+    # to bf16 1.0, alpha = v), so the stored bf16 is the rounding of v itself
+    g = json.load(open(os.path.join(GOLD, "bf16_rounding.json")))
+    cases = g["cases"]
+    alpha = np.array([int(c["f32"], 16) for c in cases], dtype=np.uint32).view(np.float32)
+    C = np.array([[0x3f80]], dtype=np.uint16)
+    f = np.zeros(len(cases), dtype=np.int32)
+    _, xt = orc.decompress(C, f, alpha)
+    for c, got in zip(cases, xt[:, 0]):
+        if c["bf16"] == "nan":
+            assert _is_nan_bf16(got), (c, hex(int(got)))
+        else:
+            assert int(got) == int(c["bf16"], 16), (c, hex(int(got)))
+
+
+def test_reconstruction_rounding_matches_torch():
+    # random bf16 generators times random fp32 scales, many products landing
+    # exactly on a rounding tie, plus overflow, subnormal and NaN products.
+    # Expected: numpy's fp32 product (one IEEE rounding) converted by torch's
+    # CPU float32 -> bfloat16 conversion (round to nearest even); neither shares
+    # code with the oracle.
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    k, d, n = 16, 64, 600
+    cbits = rng.integers(0, 1 << 16, size=(k, d), dtype=np.uint32).astype(np.uint16)
+    cbits[(cbits & 0x7f80) == 0x7f80] &= 0xbfff          # finite generators (exponent not all ones)
+    cbits[0] = 0x3f80                                    # a generator of ones: product = alpha
+    cbits[1] = np.where(np.arange(d) % 2, 0x4000, 0xc080)  # powers of two: +2, -4
+    abits = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    abits[(abits & 0x7f800000) == 0x7f800000] ^= 0x40000000   # finite scales ...
+    e = rng.integers(100, 150, size=n).astype(np.uint32)      # ... mostly of moderate exponent,
+    abits[: n // 2] = (abits[: n // 2] & 0x807fffff) | (e[: n // 2] << 23)
+    ties = slice(n // 2, n // 2 + 150)                        # exact ties: low 16 bits 0x8000
+    abits[ties] = (abits[ties] & 0xffff0000) | 0x8000
+    abits[ties] = (abits[ties] & 0x807fffff) | (e[ties] << 23)
+    abits[-9:] = [0x7f7fffff, 0xff7f8000, 0x00018000, 0x80008000, 0x7fc00000, 0x7fffffff, 0x00000000, 0x80000000, 0x0001ffff]
+    alpha = abits.view(np.float32)
+    f = rng.integers(-1, k, size=n).astype(np.int32)
+    f[n // 2: n // 2 + 200] = rng.integers(0, 2, size=200)      # ties and scales through generators 0 and 1
+    f[-9:] = 0
+    _, xt = orc.decompress(cbits, f, alpha)
+    c32 = (cbits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        prod = np.where(f[:, None] >= 0, alpha[:, None] * c32[np.maximum(f, 0)], np.float32(0)).astype(np.float32)
+    want = torch.from_numpy(prod).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(prod)
+    assert np.array_equal(_is_nan_bf16(xt), nan)
+    assert np.array_equal(xt[~nan], want[~nan])
+    # the set really contains ties and overflow
+    low = prod.view(np.uint32) & 0xffff
+    assert np.count_nonzero(low == 0x8000) > 100
+    assert np.any(np.isinf(prod))
+
+
 def test_column_subset_matches_full():
     X = gauss(60, 10, 22)
     dY = gauss(60, 13, 23)
