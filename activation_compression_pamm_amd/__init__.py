@@ -18,13 +18,15 @@ import os
 
 __all__ = [
     "PammError", "F32", "BF16", "MAX_K", "load_library", "library_path", "abi_version",
-    "sample_generators", "compress", "wgrad", "decompress",
+    "sample_generators", "compress", "wgrad", "wgrad_noalloc", "decompress", "NOALLOC_SCRATCH_BYTES",
     "compress_workspace_size", "wgrad_workspace_size", "compressed_nbytes",
 ]
 
 F32 = 0
 BF16 = 1
 MAX_K = 4096
+# size of the fixed device array pamm_wgrad_noalloc uses as its workspace
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpamm.so")
@@ -46,6 +48,10 @@ _EXPORTS = {
                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]),
+    "pamm_wgrad_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p]),
     "pamm_decompress": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]),
@@ -250,6 +256,32 @@ def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: 
                                    1 if accumulate else 0, 1 if transpose_out else 0, _ptr(ws), nbytes,
                                    _stream_ptr(stream))
     _check(st, "pamm_wgrad")
+    return dW
+
+
+def wgrad_noalloc(C, f, alpha, dY, dW, *, accumulate: bool = False, transpose_out: bool = False, stream=None):
+    """wgrad through pamm_wgrad_noalloc: the library uses its fixed per-GPU
+    scratch array instead of a workspace and allocates nothing.  dW (fp32,
+    [d x d_out], or [d_out x d] with transpose_out) is supplied by the
+    caller.  Calls that may overlap on one GPU race on the shared array."""
+    torch = _torch()
+    n, d_out, lddy = _rows(dY, "dY")
+    dt = _dtype_code(dY)
+    if C.dim() != 2:
+        raise ValueError(f"wgrad_noalloc: C must be 2-D [k x d], got shape {tuple(C.shape)}")
+    if C.dtype != dY.dtype:
+        raise TypeError("C and dY must share a dtype")
+    k, d = C.shape
+    _check_triple("wgrad_noalloc", C, f, alpha, n, k, d, dY.dtype)
+    shape = (d_out, d) if transpose_out else (d, d_out)
+    if tuple(dW.shape) != shape or dW.dtype != torch.float32:
+        raise ValueError(f"dW must be float32 of shape {shape}, got {tuple(dW.shape)} {dW.dtype}")
+    _on_gpu("wgrad_noalloc", C=C, f=f, alpha=alpha, dY=dY, dW=dW)
+    _, _, lddw = _rows(dW, "dW")
+    st = load_library().pamm_wgrad_noalloc(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, _ptr(dY), d_out, lddy, dt,
+                                           _ptr(dW), lddw, 1 if accumulate else 0, 1 if transpose_out else 0,
+                                           _stream_ptr(stream))
+    _check(st, "pamm_wgrad_noalloc")
     return dW
 
 

@@ -48,6 +48,25 @@ int num_cus() {
 
 }  // namespace
 
+namespace pamm {
+
+// Argument checks of pamm_wgrad, everything except the workspace.
+int wgrad_check(const void* C, const int32_t* f, const float* alpha, int64_t n, int64_t k, int64_t d, const void* dY,
+                int64_t d_out, int64_t lddy, int dtype, const float* dW, int64_t lddw, int transpose_out) {
+    if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
+    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || d_out < 1 ||
+        d_out > kMaxRows || (n > 0 && lddy < d_out) || lddw < (transpose_out ? d : d_out))
+        return PAMM_ERR_SHAPE;
+    if (!dW || (n > 0 && (!f || !alpha || !dY)) || (k > 0 && !C)) return PAMM_ERR_NULL;
+    if (!aligned(dW, 16) || lddw % 4 != 0) return PAMM_ERR_ALIGN;
+    if (n > 0 && (!aligned(f, 4) || !aligned(alpha, 4) || !aligned(dY, 16) || lddy % per16(dtype) != 0))
+        return PAMM_ERR_ALIGN;
+    if (k > 0 && !aligned(C, 16)) return PAMM_ERR_ALIGN;
+    return PAMM_OK;
+}
+
+}  // namespace pamm
+
 extern "C" {
 
 int pamm_abi_version(void) { return PAMM_ABI_VERSION; }
@@ -63,6 +82,7 @@ const char* pamm_status_string(int status) {
         case PAMM_ERR_UNSUPPORTED: return "unsupported request";
         case PAMM_ERR_HIP: return "HIP runtime error at launch";
         case PAMM_ERR_VALUE: return "a scalar argument is out of range";
+        case PAMM_ERR_TOO_LARGE: return "the problem needs more workspace than the fixed no-allocation scratch array holds";
         default: return "unknown status";
     }
 }
@@ -171,15 +191,8 @@ size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out,
 int pamm_wgrad(const void* C, const int32_t* f, const float* alpha, int64_t n, int64_t k, int64_t d, const void* dY,
                int64_t d_out, int64_t lddy, int dtype, float* dW, int64_t lddw, int accumulate, int transpose_out,
                void* ws, size_t ws_bytes, void* stream) {
-    if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
-    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || d_out < 1 ||
-        d_out > kMaxRows || (n > 0 && lddy < d_out) || lddw < (transpose_out ? d : d_out))
-        return PAMM_ERR_SHAPE;
-    if (!dW || (n > 0 && (!f || !alpha || !dY)) || (k > 0 && !C)) return PAMM_ERR_NULL;
-    if (!aligned(dW, 16) || lddw % 4 != 0) return PAMM_ERR_ALIGN;
-    if (n > 0 && (!aligned(f, 4) || !aligned(alpha, 4) || !aligned(dY, 16) || lddy % per16(dtype) != 0))
-        return PAMM_ERR_ALIGN;
-    if (k > 0 && !aligned(C, 16)) return PAMM_ERR_ALIGN;
+    const int st = pamm::wgrad_check(C, f, alpha, n, k, d, dY, d_out, lddy, dtype, dW, lddw, transpose_out);
+    if (st != PAMM_OK) return st;
     const pamm::WgradLayout L = pamm::wgrad_layout(n, k, d, d_out);
     if (!ws || ws_bytes < L.total) return PAMM_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return PAMM_ERR_ALIGN;

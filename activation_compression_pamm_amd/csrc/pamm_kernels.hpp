@@ -85,6 +85,10 @@ struct WgradArgs {
 
 hipError_t run_wgrad(const WgradArgs& a, int dtype, hipStream_t st);
 
+// Argument checks of pamm_wgrad apart from the workspace (a pamm_status_t).
+int wgrad_check(const void* C, const int32_t* f, const float* alpha, int64_t n, int64_t k, int64_t d, const void* dY,
+                int64_t d_out, int64_t lddy, int dtype, const float* dW, int64_t lddw, int transpose_out);
+
 struct DecompressArgs {
     const void* C;
     const int32_t* f;

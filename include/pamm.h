@@ -15,7 +15,8 @@
  *   - Pointers are DEVICE pointers unless the parameter name ends in _host.
  *     The caller allocates and owns every buffer, including the workspace;
  *     the library never allocates device memory and keeps no state between
- *     calls.
+ *     calls (pamm_wgrad_noalloc aside, whose workspace is a fixed device
+ *     array the library's code object carries).
  *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
  *     stream).  Work is enqueued asynchronously; nothing synchronises.
  *   - dtype: PAMM_F32 or PAMM_BF16.  X, C, dY and the reconstruction share
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PAMM_ABI_VERSION 2
+#define PAMM_ABI_VERSION 3
 /* Largest generator count the segment sort of pamm_wgrad supports. */
 #define PAMM_MAX_K 4096
 
@@ -56,7 +57,8 @@ typedef enum {
     PAMM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
     PAMM_ERR_UNSUPPORTED = 6, /* valid request this build does not implement    */
     PAMM_ERR_HIP = 7,         /* the HIP runtime reported an error at launch    */
-    PAMM_ERR_VALUE = 8        /* a scalar argument is out of range (e.g. eps)   */
+    PAMM_ERR_VALUE = 8,       /* a scalar argument is out of range (e.g. eps)   */
+    PAMM_ERR_TOO_LARGE = 9    /* needs more than the no-allocation scratch array */
 } pamm_status_t;
 
 /* PAMM_ABI_VERSION of the loaded library. */
@@ -151,6 +153,36 @@ int pamm_wgrad(const void *C, const int32_t *f, const float *alpha,
                const void *dY, int64_t d_out, int64_t lddy, int dtype,
                float *dW, int64_t lddw, int accumulate, int transpose_out,
                void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the device array that serves as pamm_wgrad_noalloc's workspace
+ * (one copy per GPU, held until the process ends). */
+#define PAMM_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pamm_wgrad for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and errors as pamm_wgrad, without the workspace:
+ * the library uses a fixed device array of PAMM_NOALLOC_SCRATCH_BYTES
+ * instead, one per GPU, created with the library's code object and kept
+ * until the process ends.  Nothing is allocated or freed by this call.
+ *
+ * Errors: those of pamm_wgrad; PAMM_ERR_TOO_LARGE (nothing enqueued) when
+ * pamm_wgrad_workspace_size(n, k, d, d_out, dtype) exceeds
+ * PAMM_NOALLOC_SCRATCH_BYTES (36 MiB are needed for 32768 tokens, 6144
+ * outputs and 1024 generators, 31 MiB for 131072 tokens, 6144 outputs and
+ * 256 generators); PAMM_ERR_HIP if the array's device address cannot be
+ * obtained.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that may overlap on one GPU (different streams, or host
+ * threads without ordering) race on it and must be serialised by the
+ * caller.  Calls on one stream are ordered and safe.
+ */
+int pamm_wgrad_noalloc(const void *C, const int32_t *f, const float *alpha,
+                       int64_t n, int64_t k, int64_t d,
+                       const void *dY, int64_t d_out, int64_t lddy, int dtype,
+                       float *dW, int64_t lddw, int accumulate, int transpose_out,
+                       void *stream);
 
 /*
  * Reconstruction X~_i = alpha_i * C_f(i) (page section 2 "Metodologia",

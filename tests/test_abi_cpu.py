@@ -19,7 +19,7 @@ from oracle import oracle as orc
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pamm.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EUNSUP, EHIP, EVALUE = range(9)
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EUNSUP, EHIP, EVALUE, ETOOLARGE = range(10)
 FAKE = 0x10000  # an aligned, never-dereferenced address
 
 
@@ -36,15 +36,15 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for name in names:
         assert hasattr(lib, name), name
         assert name in pamm._EXPORTS, f"binding does not wrap {name}"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pamm_abi_version() == 2
-    for s in range(9):
+    assert lib.pamm_abi_version() == 3
+    for s in range(10):
         assert lib.pamm_status_string(s)
     assert lib.pamm_status_string(12345) == b"unknown status"
 
@@ -139,6 +139,33 @@ def test_wgrad_validation(lib):
     assert call_wgrad(lib, tr=1, d=64, lddw=48) == ESHAPE
     assert call_wgrad(lib, tr=1, d=32, lddw=30) == ESHAPE
     assert call_wgrad(lib, tr=1, d=32, lddw=34) == EALIGN
+
+
+def test_wgrad_noalloc_validation(lib):
+    # the no-allocation call checks every argument, then the size against its
+    # fixed scratch array, before it looks up any device
+    def call(C=FAKE, f=FAKE, a=FAKE, n=64, k=4, d=32, dY=FAKE, dout=48, lddy=48, dt=1, dW=FAKE, lddw=48, tr=0):
+        return lib.pamm_wgrad_noalloc(C, f, a, n, k, d, dY, dout, lddy, dt, dW, lddw, 0, tr, None)
+    assert call(dt=2) == EDTYPE
+    assert call(k=65) == ESHAPE
+    assert call(lddw=40) == ESHAPE
+    assert call(dW=None) == ENULL
+    assert call(dY=FAKE + 2) == EALIGN
+    assert call(tr=1, d=64, lddw=48) == ESHAPE
+    # 65536 tokens x 12288 outputs with 4096 generators needs ~274 MiB
+    big = dict(n=65536, k=4096, d=4096, dout=12288, lddy=12288, lddw=12288)
+    assert lib.pamm_wgrad_workspace_size(65536, 4096, 4096, 12288, 1) > pamm.NOALLOC_SCRATCH_BYTES
+    assert call(**big) == ETOOLARGE
+    assert lib.pamm_status_string(ETOOLARGE).startswith(b"the problem needs more workspace")
+    # the largest workloads of the benchmark configurations fit
+    for n, k, d, dout in ((32768, 1024, 2048, 6144), (131072, 256, 4096, 6144), (32768, 64, 4096, 12288)):
+        assert lib.pamm_wgrad_workspace_size(n, k, d, dout, 1) <= pamm.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PAMM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pamm.NOALLOC_SCRATCH_BYTES
 
 
 def test_decompress_validation(lib):
