@@ -25,6 +25,9 @@ product with B~ split into two bf16 terms, about 2^-17 relative).
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -34,6 +37,38 @@ from oracle import oracle as orc
 U = 2.0 ** -24
 TOL = {"bf16": 1e-2, "f32": 1e-5}
 TIGHT = {"bf16": 1e-4, "f32": 1e-5}
+
+
+# host threads for the oracle: its C calls release the GIL, so row or column
+# chunks run in parallel (the GPU machines give one GPU a 16-core share)
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_compress(X: np.ndarray, gen_idx: np.ndarray, eps: float, rows: np.ndarray | None = None) -> dict:
+    """orc.compress(..., want_scores=True) over `rows` (all rows if None),
+    split into row chunks computed by a thread pool."""
+    sel = np.arange(X.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    if sel.size < 4096 or ORACLE_THREADS == 1:
+        return orc.compress(X, gen_idx, eps, rows=sel, want_scores=True)
+    parts = np.array_split(sel, 4 * ORACLE_THREADS)
+    with cf.ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        outs = list(ex.map(lambda r: orc.compress(X, gen_idx, eps, rows=r, want_scores=True), parts))
+    res = {key: np.concatenate([o[key] for o in outs]) for key in ("f", "alpha", "cos", "margin", "scores")}
+    res["C"] = outs[0]["C"]
+    return res
+
+
+def oracle_wgrad(C: np.ndarray, f: np.ndarray, a: np.ndarray, dY: np.ndarray,
+                 cols: np.ndarray | None = None) -> np.ndarray:
+    """orc.wgrad over output columns `cols` (all if None), split into column
+    chunks computed by a thread pool."""
+    sel = np.arange(dY.shape[1]) if cols is None else np.asarray(cols, dtype=np.int64)
+    if sel.size < 256 or ORACLE_THREADS == 1:
+        return orc.wgrad(C, f, a, dY, cols=sel)
+    parts = np.array_split(sel, 2 * ORACLE_THREADS)
+    with cf.ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        outs = list(ex.map(lambda c: orc.wgrad(C, f, a, dY, cols=c), parts))
+    return np.concatenate(outs, axis=1)
 
 
 def band(d: int) -> float:
@@ -81,14 +116,15 @@ def run_gpu(X: np.ndarray, dY: np.ndarray | None, gen_idx: np.ndarray, eps: floa
 
 
 def check_compress(X: np.ndarray, gen_idx: np.ndarray, eps: float, C_g: np.ndarray, f_g: np.ndarray,
-                   a_g: np.ndarray, rows: np.ndarray | None = None) -> dict:
-    """Apply the index and alpha rules on `rows` (all rows if None)."""
+                   a_g: np.ndarray, rows: np.ndarray | None = None, return_oracle: bool = False):
+    """Apply the index and alpha rules on `rows` (all rows if None).  Returns
+    summary statistics (and, with return_oracle, the oracle's f and alpha)."""
     dt = dtype_name(X)
     n, d = X.shape
     k = gen_idx.size
     # C is an exact copy of the generator rows
     assert np.array_equal(C_g, X[gen_idx]), "C differs from X[gen_idx]"
-    r = orc.compress(X, gen_idx, eps, rows=rows, want_scores=True)
+    r = oracle_compress(X, gen_idx, eps, rows=rows)
     sel = np.arange(n) if rows is None else np.asarray(rows)
     fg, ag = f_g[sel], a_g[sel]
     fo, ao = r["f"], r["alpha"]
@@ -124,15 +160,16 @@ def check_compress(X: np.ndarray, gen_idx: np.ndarray, eps: float, C_g: np.ndarr
         da = np.abs(ag[same].astype(np.float64) - ao[same])
         worst = np.argmax(da / lim)
         assert np.all(da <= lim), f"alpha row {sel[same][worst]}: |da| {da[worst]:.3e} > {lim[worst]:.3e}"
-    return {"inband_mismatches": int(inband.size), "rows": int(sel.size), "kept": float((fg >= 0).mean()),
-            "alpha_rel": err_alpha}
+    stats = {"inband_mismatches": int(inband.size), "rows": int(sel.size), "kept": float((fg >= 0).mean()),
+             "alpha_rel": err_alpha}
+    return (stats, fo, ao) if return_oracle else stats
 
 
 def check_wgrad(C_g: np.ndarray, f_g: np.ndarray, a_g: np.ndarray, dY: np.ndarray, dW_g: np.ndarray,
                 cols: np.ndarray | None = None) -> float:
     """dW from the GPU against the oracle's wgrad fed the GPU's triple."""
     dt = dtype_name(dY)
-    ref = orc.wgrad(C_g, f_g, a_g, dY, cols=cols)
+    ref = oracle_wgrad(C_g, f_g, a_g, dY, cols=cols)
     got = dW_g if cols is None else dW_g[:, cols]
     if np.linalg.norm(ref) == 0:
         assert np.all(got == 0)
