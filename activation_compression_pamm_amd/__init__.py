@@ -139,10 +139,12 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
 
-def sample_generators(n: int, k: int, seed: int):
-    """k distinct row ids of [0, n), ascending, drawn on the host (int32 CPU tensor)."""
+def sample_generators(n: int, k: int, seed: int, *, pin: bool = False):
+    """k distinct row ids of [0, n), ascending, drawn on the host (int32 CPU
+    tensor; in page-locked memory with ``pin``, so that its upload can be
+    asynchronous)."""
     torch = _torch()
-    out = torch.empty(max(k, 0), dtype=torch.int32)
+    out = torch.empty(max(k, 0), dtype=torch.int32, pin_memory=pin)
     _check(load_library().pamm_sample_generators(n, k, seed & (2**64 - 1), _ptr(out)), "pamm_sample_generators")
     return out
 

@@ -43,8 +43,12 @@ class PammLinearFunction(torch.autograd.Function):
         X2 = X.reshape(-1, d)
         if not X2.is_contiguous():
             X2 = X2.contiguous()
+        # generators: drawn on the host into page-locked memory and uploaded
+        # asynchronously ahead of the projection, so the upload neither syncs
+        # the stream nor waits behind the GEMM (torch keeps the host buffer
+        # alive until the copy has run)
+        gen = sample_generators(X2.shape[0], k, seed, pin=True).to(X.device, non_blocking=True)
         Y = torch.nn.functional.linear(X2, W, b)
-        gen = sample_generators(X2.shape[0], k, seed).to(X.device)
         C, f, alpha = compress(X2, gen, eps)
         ctx.save_for_backward(C, f, alpha, W)
         ctx.has_bias = b is not None

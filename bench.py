@@ -7,8 +7,11 @@ pamm_wgrad (counting sort of kept rows, alpha-weighted segmented reduction,
 generator product) on the llama-7B QKV workload (n = 16 x 2048 tokens,
 d = 4096, d_out = 3 x 4096, k = 64 generators (512x), eps = 0.1, bf16),
 with every input resident in HBM before timing starts.  Two input batches
-alternate so that no step finds its inputs in the memory-side cache.
-Generator sets for all steps are drawn on the host beforehand and uploaded.
+alternate so that no step finds its inputs in the memory-side cache.  Each
+step also draws its own generator set on the host (a new seed per step) into
+page-locked memory and uploads it on the stream without a sync: the draw
+overlaps the GPU's work on earlier steps, the upload (a few microseconds)
+sits on the GPU timeline before compress.
 
 The default times 2000 steps (about 0.3 s): under this load the core clock
 dips for the first few milliseconds after the GPU leaves idle and recovers
@@ -17,8 +20,8 @@ after about a hundred steps, so a window of 100 steps reads mostly the dip
 
 Prints one JSON line: tokens/s for the whole job, per-call times, a roofline
 entry for the dominant kernel (HIP events around its launches on the stream
-it runs on) and the CPU oracle timed on a bounded sample of the same
-workload (cpu_baseline).  An event record costs the GPU a few microseconds,
+it runs on) and the CPU oracle timed on the whole step on the host's
+cores (cpu_baseline).  An event record costs the GPU a few microseconds,
 so events bracket the calls of every --sample-every'th timed step only, and
 each such step also records an empty event pair whose interval (the cost of
 the event packets themselves) is subtracted from the per-call intervals.
@@ -53,8 +56,8 @@ def parse():
     p.add_argument("--sample-every", type=int, default=10,
                    help="record per-call HIP events on every this many'th timed step")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle's timed sample")
-    p.add_argument("--cpu-cols", type=int, default=6144, help="dW columns of the oracle's timed sample")
+    p.add_argument("--cpu-threads", type=int, default=max(1, min(16, os.cpu_count() or 1)),
+                   help="host threads for the oracle's timing (default: the host's cores, at most 16)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (known bytes) to scale memory counters")
     return p.parse_args()
@@ -87,37 +90,48 @@ def algorithmic(p, kept):
     return compress_bytes, compress_flops, reduce_bytes, product_bytes, product_flops
 
 
-def cpu_baseline(X, dY, gen_idx, p, rows, cols):
-    """Time the oracle (single-threaded C, fp64) on a bounded sample and scale
-    it to the full step: compress on `rows` rows, the B~ sums of those rows on
-    `cols` output columns, and the generator product on `cols` columns."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(X, dY, gen_idx, p, threads):
+    """Time the oracle (plain C, fp64) on the host cores over the whole step:
+    compress of every row (row chunks) and the B~ sums plus generator product
+    of every output column (column chunks), the chunks spread over a pool of
+    `threads` threads.  The oracle's C calls release the GIL."""
+    import concurrent.futures as cf
+
     import numpy as np
     from oracle import oracle as orc
 
     n, dout = p["n"], p["d_out"]
-    rng = np.random.default_rng(0)
-    R = np.sort(rng.choice(n, rows, replace=False))
-    Q = np.sort(rng.choice(dout, cols, replace=False))
-    t0 = time.perf_counter()
-    r = orc.compress(X, gen_idx, p["eps"], rows=R)
-    t1 = time.perf_counter()
-    C = r["C"]
-    orc.wgrad(C, r["f"], r["alpha"], np.ascontiguousarray(dY[R]), cols=Q)
-    t2 = time.perf_counter()
-    empty = np.zeros(0, dtype=np.int32)
-    orc.wgrad(C, empty, np.zeros(0, dtype=np.float32), np.zeros((0, dout), dtype=dY.dtype), cols=Q)
-    t3 = time.perf_counter()
-    t_comp, t_w, t_prod = t1 - t0, t2 - t1, t3 - t2
-    t_sum = max(t_w - t_prod, 0.0)
-    est = t_comp * (n / rows) + t_sum * (n / rows) * (dout / cols) + t_prod * (dout / cols)
+    rows = np.array_split(np.arange(n), 8 * threads)
+    cols = np.array_split(np.arange(dout), 4 * threads)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        parts = list(ex.map(lambda r: orc.compress(X, gen_idx, p["eps"], rows=r), rows))
+        t1 = time.perf_counter()
+        C = parts[0]["C"]
+        f = np.concatenate([q["f"] for q in parts])
+        a = np.concatenate([q["alpha"] for q in parts])
+        list(ex.map(lambda c: orc.wgrad(C, f, a, dY, cols=c), cols))
+        t2 = time.perf_counter()
+    est = t2 - t0
     return {
         "value": n / est,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"compress of {rows} of {n} rows, B~ sums of those rows on {cols} of {dout} output columns, "
-                   f"generator product on {cols} columns; each part scaled to the full step "
-                   f"(measured {t_comp + t_w + t_prod:.1f} s, estimated full step {est:.1f} s)"),
+        "cpu_model": cpu_model(),
+        "sample": (f"the whole step (compress of all {n} rows, wgrad of all {dout} output columns) on {threads} "
+                   f"threads: compress {t1 - t0:.2f} s, wgrad {t2 - t1:.2f} s"),
     }
 
 
@@ -156,11 +170,6 @@ def main():
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(12345)).cuda()
     Xb = [Xd, Xd[perm].contiguous()]
     dYb = [dYd, dYd[perm].contiguous()]
-    nsets = args.warmup + args.steps
-    t_s0 = time.perf_counter()
-    gens_host = [pamm.sample_generators(n, k, synth.generator_seed(name) + i) for i in range(nsets)]
-    t_sample = (time.perf_counter() - t_s0) / nsets
-    gens = torch.stack(gens_host).cuda()
     dt_code = pamm.BF16 if p["dtype"] == "bf16" else pamm.F32
     C = torch.empty((k, d), dtype=Xd.dtype, device="cuda")
     f = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -169,11 +178,19 @@ def main():
     cws = torch.empty(max(pamm.compress_workspace_size(n, d, k, dt_code), 1), dtype=torch.uint8, device="cuda")
     wws = torch.empty(pamm.wgrad_workspace_size(n, k, d, dout, dt_code), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    host_sampling = []             # seconds per generator draw (a1), every step
 
     def step(i, ev=None):
+        """One pass of the whole path for step i: draw its generator set on
+        the host into page-locked memory (a new seed per step), upload it on
+        the stream without a sync, compress, wgrad."""
+        t = time.perf_counter()
+        gh = pamm.sample_generators(n, k, synth.generator_seed(name) + i, pin=True)
+        host_sampling.append(time.perf_counter() - t)
+        gd = gh.to("cuda", non_blocking=True)
         if ev is not None:
             ev[0].record(stream)
-        pamm.compress(Xb[i % 2], gens[i], eps, C=C, f=f, alpha=a, workspace=cws)
+        pamm.compress(Xb[i % 2], gd, eps, C=C, f=f, alpha=a, workspace=cws)
         if ev is not None:
             ev[1].record(stream)
         pamm.wgrad(C, f, a, dYb[i % 2], dW=dW, workspace=wws)
@@ -185,6 +202,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    host_sampling.clear()
     kept = float((f >= 0).float().mean().item())
 
     # sampled steps sit mid-window: the first timed step follows a host sync,
@@ -242,7 +260,7 @@ def main():
             "wgrad_us": round(t_wgrad * 1e3, 2),
             "wgrad_alg_gbs": round((rb + pb) / (t_wgrad * 1e-3) / 1e9, 1),
             "kept_fraction": round(kept, 4),
-            "host_sampling_us": round(t_sample * 1e6, 2),
+            "host_sampling_us": round(1e6 * sum(host_sampling) / max(1, len(host_sampling)), 2),
             "host_submit_us_per_step": round(t_submit * 1e6 / args.steps, 2),
             "event_sampled_steps": len(evs),
             "event_pair_us_subtracted": round(t_event * 1e3, 2),
@@ -250,7 +268,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(X, dY, gens_host[0].numpy(), p, args.cpu_rows, args.cpu_cols)
+        g0 = pamm.sample_generators(n, k, synth.generator_seed(name) + args.warmup).numpy()
+        out["cpu_baseline"] = cpu_baseline(X, dY, g0, p, args.cpu_threads)
     print(json.dumps(out), flush=True)
 
 
