@@ -18,7 +18,8 @@ import os
 
 __all__ = [
     "PammError", "F32", "BF16", "MAX_K", "load_library", "library_path", "abi_version",
-    "sample_generators", "compress", "wgrad", "wgrad_noalloc", "decompress", "NOALLOC_SCRATCH_BYTES",
+    "sample_generators", "compress", "forward_compress", "wgrad", "wgrad_noalloc", "decompress",
+    "NOALLOC_SCRATCH_BYTES", "forward_compress_workspace_size",
     "compress_workspace_size", "wgrad_workspace_size", "compressed_nbytes",
 ]
 
@@ -52,6 +53,13 @@ _EXPORTS = {
                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_void_p]),
+    "pamm_forward_compress_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                               ctypes.c_int]),
+    "pamm_forward_compress": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pamm_decompress": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]),
@@ -227,6 +235,53 @@ def compress(X, gen_idx, eps: float, *, C=None, f=None, alpha=None, workspace=No
                                       _ptr(alpha), _ptr(ws), nbytes, _stream_ptr(stream))
     _check(st, "pamm_compress")
     return C, f, alpha
+
+
+def forward_compress_workspace_size(n: int, d: int, k: int, dtype: int = BF16) -> int:
+    return int(load_library().pamm_forward_compress_workspace_size(n, d, k, dtype))
+
+
+def forward_compress(X, W, gen_idx, eps: float, *, bias=None, Y=None, C=None, f=None, alpha=None, workspace=None,
+                     stream=None):
+    """The projection Y = X W^T (+ bias) and the compression of X in one pass
+    over X (bf16 only).  X [n x d], W [d_out x d] (the layout of a linear
+    layer's weight), bias [d_out] or None, gen_idx int32 [k] on the device.
+    Returns (Y [n x d_out] bf16, C [k x d], f [n] int32, alpha [n] fp32)."""
+    torch = _torch()
+    n, d, ldx = _rows(X, "X")
+    dt = _dtype_code(X)
+    d_out, dw, ldw = _rows(W, "W")
+    if dw != d:
+        raise ValueError(f"forward_compress: W must be [d_out x {d}], got {tuple(W.shape)}")
+    if W.dtype != X.dtype:
+        raise TypeError("forward_compress: X and W must share a dtype")
+    if bias is not None:
+        _need("forward_compress", "bias", bias, (d_out,), X.dtype)
+    if gen_idx.dim() != 1:
+        raise ValueError(f"forward_compress: gen_idx must be 1-D, got shape {tuple(gen_idx.shape)}")
+    k = gen_idx.numel()
+    _check_triple("forward_compress", C, f, alpha, n, k, d, X.dtype)
+    _check_workspace("forward_compress", workspace)
+    if Y is not None and (tuple(Y.shape) != (n, d_out) or Y.dtype != X.dtype):
+        raise ValueError(f"Y must be {X.dtype} of shape {(n, d_out)}, got {tuple(Y.shape)} {Y.dtype}")
+    _on_gpu("forward_compress", X=X, W=W, bias=bias, Y=Y, C=C, f=f, alpha=alpha, workspace=workspace)
+    gen_idx = gen_idx.to(device=X.device, dtype=torch.int32).contiguous()
+    if Y is None:
+        Y = torch.empty((n, d_out), dtype=X.dtype, device=X.device)
+    _, _, ldy = _rows(Y, "Y")
+    if C is None:
+        C = torch.empty((k, d), dtype=X.dtype, device=X.device)
+    if f is None:
+        f = torch.empty(n, dtype=torch.int32, device=X.device)
+    if alpha is None:
+        alpha = torch.empty(n, dtype=torch.float32, device=X.device)
+    ws = _workspace(forward_compress_workspace_size(n, d, k, dt), X.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load_library().pamm_forward_compress(_ptr(X), n, d, ldx, dt, _ptr(W), d_out, ldw, _ptr(bias), _ptr(Y), ldy,
+                                              _ptr(gen_idx), k, float(eps), _ptr(C), _ptr(f), _ptr(alpha), _ptr(ws),
+                                              nbytes, _stream_ptr(stream))
+    _check(st, "pamm_forward_compress")
+    return Y, C, f, alpha
 
 
 def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: bool = False, workspace=None,

@@ -182,6 +182,90 @@ int pamm_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int dtype, c
     return e == hipSuccess ? PAMM_OK : PAMM_ERR_HIP;
 }
 
+// Workspace of pamm_forward_compress: |c_j|^2 [k] always, plus per-tile
+// winners and |x|^2 when k > 256.
+namespace {
+struct ForwardLayout {
+    size_t off_partial, off_xn2, off_cn2, total;
+};
+ForwardLayout forward_layout(int64_t n, int64_t k) {
+    ForwardLayout L{0, 0, 0, 0};
+    size_t off = 0;
+    if (k > pamm::kMaxTileGens) {
+        const int64_t ntiles = (k + pamm::kMaxTileGens - 1) / pamm::kMaxTileGens;
+        L.off_partial = off;
+        off += up256(sizeof(pamm::PartialBest) * (size_t)(ntiles * n));
+        L.off_xn2 = off;
+        off += up256(sizeof(float) * (size_t)n);
+    }
+    L.off_cn2 = off;
+    off += up256(sizeof(float) * (size_t)(k > 0 ? k : 1));
+    L.total = off;
+    return L;
+}
+}  // namespace
+
+size_t pamm_forward_compress_workspace_size(int64_t n, int64_t d, int64_t k, int dtype) {
+    (void)d;
+    (void)dtype;
+    if (n < 0 || k < 0) return 0;
+    return forward_layout(n, k).total;
+}
+
+int pamm_forward_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int dtype, const void* W, int64_t d_out,
+                          int64_t ldw, const void* bias, void* Y, int64_t ldy, const int32_t* gen_idx, int64_t k,
+                          float eps, void* C, int32_t* f, float* alpha, void* ws, size_t ws_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
+    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || ldx < d ||
+        d_out < 1 || d_out > kMaxRows || ldw < d || ldy < d_out)
+        return PAMM_ERR_SHAPE;
+    if (!(eps >= 0.0f) || isinf(eps)) return PAMM_ERR_VALUE;
+    if (dtype != PAMM_BF16) return PAMM_ERR_UNSUPPORTED;
+    if (n == 0) return PAMM_OK;
+    if (!X || !W || !Y || !f || !alpha || (k > 0 && (!gen_idx || !C))) return PAMM_ERR_NULL;
+    if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(W, 16) || ldw % 8 != 0 || !aligned(Y, 16) || ldy % 8 != 0 ||
+        (bias && !aligned(bias, 2)) || !aligned(f, 4) || !aligned(alpha, 4) ||
+        (k > 0 && (!aligned(gen_idx, 4) || !aligned(C, 16))))
+        return PAMM_ERR_ALIGN;
+    // the kernel addresses X and W with 32-bit offsets from a base
+    if ((uint64_t)n * (uint64_t)ldx * 2u + 256u > 0xffffffffull ||
+        (uint64_t)d_out * (uint64_t)ldw * 2u + 256u > 0xffffffffull)
+        return PAMM_ERR_UNSUPPORTED;
+    const ForwardLayout L = forward_layout(n, k);
+    if (!ws || ws_bytes < L.total) return PAMM_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return PAMM_ERR_ALIGN;
+
+    pamm::CompressArgs a;
+    memset(&a, 0, sizeof a);
+    a.X = X;
+    a.n = n;
+    a.d = d;
+    a.ldx_bytes = ldx * 2;
+    a.row_bytes = d * 2;
+    a.gen_idx = gen_idx;
+    a.k = (int)k;
+    a.eps = eps;
+    a.C = C;
+    a.c_vec_ok = (d * 2) % 16 == 0;
+    a.f = f;
+    a.alpha = alpha;
+    a.num_cus = num_cus();
+    char* w = reinterpret_cast<char*>(ws);
+    if (k > pamm::kMaxTileGens) {
+        a.partial = reinterpret_cast<pamm::PartialBest*>(w + L.off_partial);
+        a.xn2 = reinterpret_cast<float*>(w + L.off_xn2);
+    }
+    a.cn2 = reinterpret_cast<float*>(w + L.off_cn2);
+    a.W = W;
+    a.ldw_bytes = ldw * 2;
+    a.d_out = d_out;
+    a.Y = Y;
+    a.ldy_bytes = ldy * 2;
+    a.bias = bias;
+    const hipError_t e = pamm::run_forward_compress(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PAMM_OK : PAMM_ERR_HIP;
+}
+
 size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out, int dtype) {
     (void)dtype;
     if (n < 0 || k < 0 || d < 1 || d_out < 1) return 0;

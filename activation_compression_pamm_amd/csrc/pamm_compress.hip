@@ -496,9 +496,75 @@ __device__ __forceinline__ float sumsq_dot2(const v4u32& v, float acc) {
     return acc;
 }
 
+// Epilogue of a Y tile (pamm_forward_compress): each wave's 32*MT x 32*NT
+// block of X W^T, plus the bias, rounded to bf16 (nearest even), goes to Y
+// through LDS in passes of 32 rows (each lane writes its 2-byte values, then
+// every lane stores whole 16-byte pieces of the staged rows; non-temporal:
+// Y is not re-read by this pass).  Rows past n and columns past d_out are not written.
+// Element i of a 32x32 result lane l is row 8*(i/4) + 4*(l/32) + i%4,
+// column l%32.
+template <int MT, int NT, int NWR, int NWC>
+__device__ __forceinline__ void store_y_tile(const CompressArgs& a, const f32x16 (&acc)[MT][NT], char* ring,
+                                             int64_t m0, int64_t n0, int wr, int wc, int lane, int wave) {
+    constexpr int WM = 32 * MT, WN = 32 * NT;
+    constexpr int PITCH = WN * 2 + 16;     // bytes per staged row: 16 banks apart for rows 4 apart
+    constexpr int CH = WN * 2 / 16;        // 16-byte pieces per staged row
+    static_assert((64 % CH) == 0, "pieces of a staged row divide the wave");
+    constexpr int RPI = 64 / CH;           // rows read per instruction
+    char* buf = ring + wave * 32 * PITCH;
+    const int frow = lane & 31, fk = lane >> 5;
+    const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.bias);
+    float bv[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int64_t col = n0 + wc * WN + nt * 32 + frow;
+        bv[nt] = (bias && col < a.d_out) ? bf16_to_f32(bias[col]) : 0.f;
+    }
+    const int64_t col0 = n0 + wc * WN;
+    char* Y = reinterpret_cast<char*>(a.Y);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 8 * (i >> 2) + 4 * fk + (i & 3);
+                *reinterpret_cast<uint16_t*>(buf + r * PITCH + (nt * 32 + frow) * 2) =
+                    (uint16_t)f32_to_bf16(acc[mt][nt][i] + bv[nt]);
+            }
+        __syncthreads();
+        const int q = lane % CH;
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int r = lane / CH + RPI * it;
+            const int64_t row = m0 + wr * WM + mt * 32 + r;
+            const int64_t col = col0 + q * 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(buf + r * PITCH + q * 16);
+            if (row < a.n && col < a.d_out) {
+                char* dst = Y + row * a.ldy_bytes + col * 2;
+                if (col + 8 <= a.d_out) {
+                    __builtin_nontemporal_store(v4u32{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32*>(dst));
+                } else {
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                    for (int e = 0; col + e < a.d_out; ++e)
+                        reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // MASKED: the tail stage and padding positions exist (d not a multiple of 64,
 // or an odd stage count); without them the stash applies no masks.
-template <int MT, int NT, int NWR, int NWC, bool MASKED>
+// FUSED: the forward projection Y = X W^T (+ bias) runs in the same launch.
+// Its 256-column tiles are extra column tiles in front of the generator
+// tiles: their B operand rows are rows of W instead of generator rows of X,
+// the main loop is the same, and their epilogue stores the bf16 tile of Y.
+// Workgroups take (row block, column tile) pairs in groups of 4 row blocks x
+// 8 column tiles, one group per XCD at a time, so that the 32 workgroups an
+// XCD runs together share their X and W panels in its L2.
+template <int MT, int NT, int NWR, int NWC, bool MASKED, bool FUSED = false>
 __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressArgs a) {
     constexpr int RB = 128;                 // bytes of a row per stage
     constexpr int E = RB / 2;               // elements per stage
@@ -529,14 +595,33 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // workgroup -> (row block, generator tile), as in compress_rs_kernel
     int64_t rb = blockIdx.x;
     int tile = 0;
-    if (a.ntiles > 1) {
+    bool wtile = false;  // FUSED: a column tile of Y (B rows from W)
+    int64_t n0 = 0;      // FUSED: first output column of a Y tile
+    if constexpr (FUSED) {
+        // block b runs on XCD b % 8; the XCD's slots s = b / 8 take groups of
+        // 32: group p = (s / 32) * 8 + XCD, inside it 4 row blocks x 8 tiles
+        const int64_t b = blockIdx.x, s = b >> 3;
+        const int64_t p = (s >> 5) * 8 + (b & 7);
+        const int w = (int)(s & 31);
+        const int64_t nct = (int64_t)a.tiles_w + a.ntiles, nqc = (nct + 7) / 8;
+        rb = (p / nqc) * 4 + (w & 3);
+        const int64_t ct = (p % nqc) * 8 + (w >> 2);
+        if (ct >= nct) return;  // slot past the last column tile (whole workgroup)
+        if (ct < a.tiles_w) {
+            wtile = true;
+            n0 = ct * BN;
+        } else {
+            tile = (int)(ct - a.tiles_w);
+        }
+    } else if (a.ntiles > 1) {
         const int64_t grp = blockIdx.x / (8 * a.ntiles), rem = blockIdx.x % (8 * a.ntiles);
         tile = (int)(rem / 8);
         rb = grp * 8 + rem % 8;
     }
     const int64_t m0 = rb * BM;
     const int gen0 = tile * BN;
-    const int ktile = min(BN, a.k - gen0);
+    // B operand rows of this tile that exist: generators, or columns of Y
+    const int ktile = FUSED && wtile ? (int)min((int64_t)BN, a.d_out - n0) : min(BN, a.k - gen0);
     const int nst = (int)((a.d + E - 1) / E);
     const int npos = (nst + 1) & ~1;        // stage positions, padded to even
     const int last = nst - 1;
@@ -560,10 +645,15 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int jj = min((NTH / 8) * i + rsub, ktile - 1);  // padding generators: any valid one, masked later
-        int64_t g = a.gen_idx[gen0 + jj];
-        g = g < 0 ? 0 : (g >= a.n ? a.n - 1 : g);
-        coff[i] = (uint32_t)(g * a.ldx_bytes);
+        if (FUSED && wtile) {
+            coff[i] = (uint32_t)((n0 + jj) * a.ldw_bytes);  // padding columns of Y: a valid row of W, unused
+        } else {
+            int64_t g = a.gen_idx[gen0 + jj];
+            g = g < 0 ? 0 : (g >= a.n ? a.n - 1 : g);
+            coff[i] = (uint32_t)(g * a.ldx_bytes);
+        }
     }
+    const char* __restrict__ Bsrc = FUSED && wtile ? reinterpret_cast<const char*>(a.W) : X;
     // LDS slot of load i: row (NTH/8)*i + rsub, chunk qc swizzled by the
     // row's key (the same for every i, so slot i is slot 0 plus a constant)
     const int dst0 = rsub * RB + ((qc ^ gemm_swz_key(rsub)) << 4);
@@ -602,7 +692,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             for (int i = 4 * part; i < 4 * part + 4; ++i)
                 xr[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(bx + (xoff[i] + q16)));
         } else {
-            const char* bc = X + (int64_t)st * RB;
+            const char* bc = Bsrc + (int64_t)st * RB;
 #pragma unroll
             for (int i = 4 * (part - XP); i < 4 * (part - XP) + 4; ++i)
                 cr[i] = *reinterpret_cast<const v4u32*>(bc + (coff[i] + q16));
@@ -772,7 +862,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
         body(p, s_tile, s_tile + TILE, wx);
         tail(s_tile + TILE);
     };
-    if (tile == 0)
+    if (tile == 0 && !(FUSED && wtile))
         run(std::true_type{});
     else
         run(std::false_type{});
@@ -780,6 +870,12 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // ---- epilogue (the stage ring is free now: every wave has passed the
     // last compute, so waves reuse it as scratch after one more barrier)
     __syncthreads();
+    if constexpr (FUSED) {
+        if (wtile) {
+            store_y_tile<MT, NT, NWR, NWC>(a, acc, s_tile, m0, n0, wr, wc, lane, wave);
+            return;
+        }
+    }
     float* ring = reinterpret_cast<float*>(s_tile);
     // norms: each lane's partial |x|^2 of its 8 rows go to LDS, one thread
     // per tile row adds the 8 chunks (zeros outside the first tile, where
@@ -1099,6 +1195,37 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
             }
             return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);
     }
+}
+
+hipError_t run_forward_compress(const CompressArgs& a0, hipStream_t st) {
+    constexpr int MT = 4, NT = 4, NWR = 2, NWC = 2, BM = 32 * MT * NWR, BN = 32 * NT * NWC;
+    CompressArgs a = a0;
+    a.ntiles = (int)((a.k + BN - 1) / BN);
+    a.tiles_w = (int)((a.d_out + BN - 1) / BN);
+    if (a.ntiles <= 1) { a.partial = nullptr; a.xn2 = nullptr; }
+    if (a.k > 0) {
+        const unsigned pblocks = (unsigned)std::min<int64_t>(a.k, 4096);
+        hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL(compress_empty_kernel, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, st, a.n, a.f,
+                           a.alpha);
+    }
+    // groups of 4 row blocks x 8 column tiles, padded to a multiple of the 8 XCDs
+    const int64_t nrb = (a.n + BM - 1) / BM;
+    const int64_t ngroups = ((nrb + 3) / 4) * ((a.tiles_w + a.ntiles + 7) / 8);
+    const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * 32));
+    const int64_t nst = (a.d + 63) / 64;
+    if (a.d % 64 != 0 || nst % 2 != 0)
+        hipLaunchKernelGGL((compress_gemm_kernel<MT, NT, NWR, NWC, true, true>), grid, dim3(64 * NWR * NWC), 0, st, a);
+    else
+        hipLaunchKernelGGL((compress_gemm_kernel<MT, NT, NWR, NWC, false, true>), grid, dim3(64 * NWR * NWC), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.ntiles <= 1) return e;
+    hipLaunchKernelGGL(compress_merge_kernel, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, st, a.partial,
+                       a.xn2, a.n, a.ntiles, a.eps, a.f, a.alpha);
+    return hipGetLastError();
 }
 
 hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st) {

@@ -47,9 +47,20 @@ struct CompressArgs {
     float* cn2;            // [k] |c_j|^2, bf16 with k > kMaxTileGens / 2 (the GEMM-shaped path)
     int ntiles;            // generator tiles (set by the launcher)
     int num_cus;           // compute units of the device
+    // the forward projection computed in the same pass (pamm_forward_compress;
+    // all zero for pamm_compress): Y [n x d_out] = X W^T (+ bias), bf16
+    const void* W;         // [d_out x d], rows ldw_bytes apart
+    int64_t ldw_bytes;
+    int64_t d_out;
+    void* Y;               // [n x d_out], rows ldy_bytes apart
+    int64_t ldy_bytes;
+    const void* bias;      // [d_out] or null
+    int tiles_w;           // 256-column tiles of Y
 };
 
 hipError_t run_compress(const CompressArgs& a, int dtype, hipStream_t st);
+// Y = X W^T (+ bias) and the compression of X in one pass (bf16 only).
+hipError_t run_forward_compress(const CompressArgs& a, hipStream_t st);
 
 // Workspace carve-up of pamm_wgrad (all offsets 256-byte aligned).
 struct WgradLayout {

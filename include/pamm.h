@@ -121,6 +121,42 @@ int pamm_compress(const void *X, int64_t n, int64_t d, int64_t ldx, int dtype,
                   void *C, int32_t *f, float *alpha,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace pamm_forward_compress needs: the generator norms
+ * |c_j|^2, plus per-tile winners and |x|^2 when k > 256. */
+size_t pamm_forward_compress_workspace_size(int64_t n, int64_t d, int64_t k, int dtype);
+
+/*
+ * The projection and the compression in one pass over X (page section 2
+ * "Metodologia", "Algoritmo in Due Fasi": the compressed form is computed
+ * during the forward pass of the QKV projection, whose input X it replaces):
+ *
+ *   Y = X W^T (+ bias)       [n x d_out], fp32 accumulation, rounded to bf16
+ *                            (nearest even) after the bias is added in fp32
+ *   (C, f, alpha)            exactly as pamm_compress defines them
+ *
+ *   X     [n x d] bf16, leading dimension ldx            (read)
+ *   W     [d_out x d] bf16, leading dimension ldw >= d   (read; the layout
+ *         of a linear layer's weight)
+ *   bias  [d_out] bf16, or NULL                          (read)
+ *   Y     [n x d_out] bf16, leading dimension ldy >= d_out (written)
+ *   gen_idx, k, eps, C, f, alpha as for pamm_compress
+ *   ws    workspace of at least pamm_forward_compress_workspace_size bytes
+ *
+ * Alignment as for pamm_compress, plus W and Y 16-byte aligned with ldw and
+ * ldy multiples of 8 elements, and bias 2-byte aligned.  Only bf16:
+ * PAMM_ERR_UNSUPPORTED for fp32, and also when n x ldx or d_out x ldw spans
+ * 4 GiB or more.  The indices and alpha follow the rules of pamm_compress's
+ * GEMM-shaped kernel (|c_j|^2 summed outside the matrix product, so a
+ * power-of-two multiple of a generator gets alpha exact to a few fp32 ulps).
+ * Deterministic.
+ */
+int pamm_forward_compress(const void *X, int64_t n, int64_t d, int64_t ldx, int dtype,
+                          const void *W, int64_t d_out, int64_t ldw, const void *bias,
+                          void *Y, int64_t ldy,
+                          const int32_t *gen_idx, int64_t k, float eps,
+                          void *C, int32_t *f, float *alpha,
+                          void *ws, size_t ws_bytes, void *stream);
+
 /* Bytes of workspace pamm_wgrad needs. */
 size_t pamm_wgrad_workspace_size(int64_t n, int64_t k, int64_t d, int64_t d_out, int dtype);
 

@@ -62,6 +62,19 @@ int main(void) {
     EXPECT(pamm_wgrad_noalloc(P(A), P(A), P(A), 64, 4, 32, P(A), 48, 48, 1, NULL, 48, 0, 0, NULL) == PAMM_ERR_NULL);
     EXPECT(pamm_wgrad_noalloc(P(A), P(A), P(A), 65536, 4096, 4096, P(A), 12288, 12288, 1, P(A), 12288, 0, 0, NULL) ==
            PAMM_ERR_TOO_LARGE);
+    /* the fused projection + compression */
+    size_t fw = pamm_forward_compress_workspace_size(64, 32, 4, PAMM_BF16);
+    EXPECT(fw > 0);
+    EXPECT(pamm_forward_compress(P(A), 64, 32, 32, 0, P(A), 48, 32, NULL, P(A), 48, P(A), 4, 0.1f, P(A), P(A), P(A),
+                                 P(A), fw, NULL) == PAMM_ERR_UNSUPPORTED);
+    EXPECT(pamm_forward_compress(P(A), 64, 32, 32, 1, NULL, 48, 32, NULL, P(A), 48, P(A), 4, 0.1f, P(A), P(A), P(A),
+                                 P(A), fw, NULL) == PAMM_ERR_NULL);
+    EXPECT(pamm_forward_compress(P(A), 64, 32, 32, 1, P(A), 48, 16, NULL, P(A), 48, P(A), 4, 0.1f, P(A), P(A), P(A),
+                                 P(A), fw, NULL) == PAMM_ERR_SHAPE);
+    EXPECT(pamm_forward_compress(P(A), 64, 32, 32, 1, P(A), 48, 32, P(A + 1), P(A), 48, P(A), 4, 0.1f, P(A), P(A),
+                                 P(A), P(A), fw, NULL) == PAMM_ERR_ALIGN);
+    EXPECT(pamm_forward_compress(P(A), 64, 32, 32, 1, P(A), 48, 32, NULL, P(A), 48, P(A), 4, 0.1f, P(A), P(A), P(A),
+                                 P(A), fw - 1, NULL) == PAMM_ERR_WORKSPACE);
     /* decompress */
     EXPECT(pamm_decompress(P(A), P(A), P(A), 64, 4, 32, 3, P(A), 32, NULL) == PAMM_ERR_DTYPE);
     EXPECT(pamm_decompress(P(A), P(A), P(A), 64, 4, 32, 1, P(A), 16, NULL) == PAMM_ERR_SHAPE);

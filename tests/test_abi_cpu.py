@@ -36,7 +36,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), name
         assert name in pamm._EXPORTS, f"binding does not wrap {name}"
@@ -166,6 +166,36 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define PAMM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == pamm.NOALLOC_SCRATCH_BYTES
+
+
+def test_forward_compress_validation(lib):
+    def call(X=FAKE, n=64, d=32, ldx=32, dt=1, W=FAKE, dout=48, ldw=32, bias=None, Y=FAKE, ldy=48, gen=FAKE, k=4,
+             eps=0.1, C=FAKE, f=FAKE, a=FAKE, ws=FAKE, wsb=None):
+        if wsb is None:
+            wsb = lib.pamm_forward_compress_workspace_size(n, d, k, dt)
+        return lib.pamm_forward_compress(X, n, d, ldx, dt, W, dout, ldw, bias, Y, ldy, gen, k, eps, C, f, a, ws, wsb,
+                                         None)
+    assert call(dt=4) == EDTYPE
+    assert call(dt=0, ldx=32) == EUNSUP          # fp32 is not offered by the fused pass
+    assert call(ldw=16) == ESHAPE
+    assert call(ldy=40) == ESHAPE
+    assert call(dout=0, ldy=0) == ESHAPE
+    assert call(k=65) == ESHAPE
+    assert call(eps=-0.5) == EVALUE
+    assert call(W=None) == ENULL
+    assert call(Y=None) == ENULL
+    assert call(W=FAKE + 8) == EALIGN
+    assert call(ldw=36) == EALIGN
+    assert call(Y=FAKE + 4) == EALIGN
+    assert call(bias=FAKE + 1) == EALIGN
+    assert call(ws=None) == EWS
+    assert call(wsb=0) == EWS
+    assert call(ws=FAKE + 32) == EALIGN
+    # 32-bit addressing of X and W: a W spanning 4 GiB is refused
+    assert call(dout=300000, ldw=8192, d=8192, ldx=8192, ldy=300000) == EUNSUP
+    assert call(n=0, k=0, X=None, gen=None, C=None, f=None, a=None, Y=None, W=None) == OK
+    assert lib.pamm_forward_compress_workspace_size(1024, 32, 300, 1) > lib.pamm_forward_compress_workspace_size(
+        1024, 32, 200, 1) > 0
 
 
 def test_decompress_validation(lib):
