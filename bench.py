@@ -7,11 +7,13 @@ pamm_wgrad (counting sort of kept rows, alpha-weighted segmented reduction,
 generator product) on the llama-7B QKV workload (n = 16 x 2048 tokens,
 d = 4096, d_out = 3 x 4096, k = 64 generators (512x), eps = 0.1, bf16),
 with every input resident in HBM before timing starts.  Two input batches
-alternate so that no step finds its inputs in the memory-side cache.  Each
-step also draws its own generator set on the host (a new seed per step) into
-page-locked memory and uploads it on the stream without a sync: the draw
-overlaps the GPU's work on earlier steps, the upload (a few microseconds)
-sits on the GPU timeline before compress.
+alternate so that no step finds its inputs in the memory-side cache.  Every
+step has its own generator set (a new seed per step).  The sets depend only on
+(n, k, seed), so they are pipelined: each step draws, on the host, the set of
+the step 16 ahead into page-locked memory, and every 16th step uploads the
+next 16 sets with one copy on the stream, without a sync.  So each timed step
+does one draw (overlapping the GPU's work) and a sixteenth of an upload (one
+upload per step would add a few microseconds of GPU timeline each).
 
 The default times 2000 steps (about 0.3 s): under this load the core clock
 dips for the first few milliseconds after the GPU leaves idle and recovers
@@ -29,6 +31,7 @@ the event packets themselves) is subtracted from the per-call intervals.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -45,6 +48,8 @@ BF16_PEAK_TFLOPS = 2500.0
 # FETCH_SIZE/WRITE_SIZE counters scaled by what they read for a plain copy of
 # known size; used while the kernel sources still match the ones profiled
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_llama7b_qkv_traffic.json")
+# generator sets uploaded together (see step() in main)
+GEN_BATCH = 16
 
 
 def parse():
@@ -179,24 +184,49 @@ def main():
     wws = torch.empty(pamm.wgrad_workspace_size(n, k, d, dout, dt_code), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     host_sampling = []             # seconds per generator draw (a1), every step
+    # a1 pipelined: step i draws the set of step i + GEN_BATCH on the host into
+    # one of two page-locked batch buffers; the last step of a batch uploads
+    # the next batch with one copy on the stream (no sync).  Before a buffer
+    # is refilled the host waits for the event of its previous upload.
+    B = GEN_BATCH
+    gen_host = torch.zeros((2, B, max(k, 1)), dtype=torch.int32, pin_memory=True)
+    gen_dev = torch.zeros((2, B, max(k, 1)), dtype=torch.int32, device="cuda")
+    uploaded = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def draw(i):
+        buf = (i // B) % 2
+        t = time.perf_counter()
+        pamm.load_library().pamm_sample_generators(n, k, synth.generator_seed(name) + i,
+                                                   ctypes.c_void_p(gen_host[buf, i % B].data_ptr()))
+        host_sampling.append(time.perf_counter() - t)
+
+    def upload(buf):
+        gen_dev[buf].copy_(gen_host[buf], non_blocking=True)
+        uploaded[buf].record(stream)
+
+    for i in range(B):
+        draw(i)
+    upload(0)
 
     def step(i, ev=None):
-        """One pass of the whole path for step i: draw its generator set on
-        the host into page-locked memory (a new seed per step), upload it on
-        the stream without a sync, compress, wgrad."""
-        t = time.perf_counter()
-        gh = pamm.sample_generators(n, k, synth.generator_seed(name) + i, pin=True)
-        host_sampling.append(time.perf_counter() - t)
-        gd = gh.to("cuda", non_blocking=True)
+        """One pass of the whole path for step i: compress with its generator
+        set, a1 for step i + GEN_BATCH on the host, wgrad (and the upload of
+        the next batch after the last step of a batch)."""
+        buf, row = (i // B) % 2, i % B
         if ev is not None:
             ev[0].record(stream)
-        pamm.compress(Xb[i % 2], gd, eps, C=C, f=f, alpha=a, workspace=cws)
+        pamm.compress(Xb[i % 2], gen_dev[buf, row, :k], eps, C=C, f=f, alpha=a, workspace=cws)
         if ev is not None:
             ev[1].record(stream)
+        if row == 0:
+            uploaded[1 - buf].synchronize()   # the other buffer's last upload has run
+        draw(i + B)
         pamm.wgrad(C, f, a, dYb[i % 2], dW=dW, workspace=wws)
         if ev is not None:
             ev[2].record(stream)
             ev[3].record(stream)
+        if row == B - 1:
+            upload(1 - buf)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
