@@ -459,8 +459,11 @@ __device__ __forceinline__ void interleave_spread() {
 // Tiles of 256 generators in bf16: the contraction dominates (k >= 256 means
 // at least 256 MFMA flops per byte of X), so the workgroup is shaped like a
 // GEMM tile: NWR x NWC waves, each holding 32*MT rows x 32*NT generators of
-// S in 32x32 MFMA accumulators (256 registers at 4 x 4: the whole
-// accumulation register file), so one LDS fragment read feeds 4 MFMAs.
+// S in 32x32 MFMA accumulators.  Two shapes of a 256 x 256 tile: 2 x 2 waves
+// of 128 x 128 (256 accumulation registers, one wave per SIMD, one LDS
+// fragment read per 2 MFMAs) and 2 x 4 waves of 128 x 64 (two waves per
+// SIMD, whose memory traffic and MFMAs overlap; a fragment read per 1.33
+// MFMAs).
 //   * One stage = 64 elements (128 bytes) of every tile row.  X and C lines
 //     are fetched as whole 128-byte lines into registers one stage ahead and
 //     written to a double-buffered LDS tile, XOR-swizzled with this kernel's
@@ -511,6 +514,8 @@ __device__ __forceinline__ void store_y_tile(const CompressArgs& a, const f32x16
     constexpr int CH = WN * 2 / 16;        // 16-byte pieces per staged row
     static_assert((64 % CH) == 0, "pieces of a staged row divide the wave");
     constexpr int RPI = 64 / CH;           // rows read per instruction
+    static_assert(NWR * NWC * 32 * PITCH <= 2 * (32 * MT * NWR + 32 * NT * NWC) * 128,
+                  "the staged Y rows fit in the stage ring");
     char* buf = ring + wave * 32 * PITCH;
     const int frow = lane & 31, fk = lane >> 5;
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.bias);
@@ -911,6 +916,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     constexpr int HW = WN / 2;         // generators scanned per lane
     constexpr int HOFF = HW + 4;       // offset of the second half
     constexpr int PST = WN + 8;        // floats per staged row
+    static_assert(NW * 32 * PST * (int)sizeof(float) <= 2 * TILE, "the staged S rows fit in the stage ring");
     float* wbuf = ring + wave * 32 * PST;
     const int sr = lane >> 1, sh = lane & 1;
     const int jl0 = wc * WN + sh * HW;  // tile index of the lane's first generator
@@ -1151,6 +1157,14 @@ static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStr
 #ifndef PAMM_COMPRESS_GEMM
 #define PAMM_COMPRESS_GEMM 4, 4, 2, 2
 #endif
+// with several generator tiles (k > 256): 2 x 4 waves of 128 rows x 64
+// generators, two waves per SIMD, so that one wave's LDS and global traffic
+// runs while the other's MFMAs do.  The X lines of a row block then come
+// from L2 (its tiles run together on one XCD); with one tile, X streams from
+// HBM and the 4-wave tile, with a third fewer LDS fragment reads, is faster.
+#ifndef PAMM_COMPRESS_GEMM_MULTI
+#define PAMM_COMPRESS_GEMM_MULTI 4, 2, 2, 4
+#endif
 // the same with 128-row blocks (2 x 2 waves of 64 rows x 128 generators), for
 // inputs whose 256-row blocks leave compute units idle
 #ifndef PAMM_COMPRESS_GEMM_HALF
@@ -1189,16 +1203,30 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
                     hipLaunchKernelGGL(gen_prep_kernel, dim3(pblocks), dim3(256), 0, st, a);
                     const hipError_t e = hipGetLastError();
                     if (e != hipSuccess) return e;
-                    return full ? launch_compress_gemm<PAMM_COMPRESS_GEMM>(a, ntiles, st)
-                                : launch_compress_gemm<PAMM_COMPRESS_GEMM_HALF>(a, ntiles, st);
+                    if (!full) return launch_compress_gemm<PAMM_COMPRESS_GEMM_HALF>(a, ntiles, st);
+                    return ntiles > 1 ? launch_compress_gemm<PAMM_COMPRESS_GEMM_MULTI>(a, ntiles, st)
+                                      : launch_compress_gemm<PAMM_COMPRESS_GEMM>(a, ntiles, st);
                 }
             }
             return launch_compress_rs<DT, PAMM_COMPRESS_RS256>(a, ntiles, st);
     }
 }
 
+// the fused pass re-reads each X panel from L2 for every column tile: the
+// 8-wave tile, as for several generator tiles
+#ifndef PAMM_FUSED_GEMM
+#define PAMM_FUSED_GEMM 4, 2, 2, 4
+#endif
+template <int MT, int NT, int NWR, int NWC>
+static hipError_t launch_forward(const CompressArgs& a0, hipStream_t st);
+
 hipError_t run_forward_compress(const CompressArgs& a0, hipStream_t st) {
-    constexpr int MT = 4, NT = 4, NWR = 2, NWC = 2, BM = 32 * MT * NWR, BN = 32 * NT * NWC;
+    return launch_forward<PAMM_FUSED_GEMM>(a0, st);
+}
+
+template <int MT, int NT, int NWR, int NWC>
+static hipError_t launch_forward(const CompressArgs& a0, hipStream_t st) {
+    constexpr int BM = 32 * MT * NWR, BN = 32 * NT * NWC;
     CompressArgs a = a0;
     a.ntiles = (int)((a.k + BN - 1) / BN);
     a.tiles_w = (int)((a.d_out + BN - 1) / BN);
