@@ -256,7 +256,7 @@ def main():
 
     cb, cf, rb, pb, pf = algorithmic(p, kept)
     comp_gbs = cb / (t_comp * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "compress_kernel (pamm_compress)", "achieved": round(comp_gbs, 1),
+    roofline = {"bound": "hbm", "kernel": "compress_rs_kernel (pamm_compress)", "achieved": round(comp_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None, "algorithmic_bytes_per_launch": cb, "avg_launch_us": round(t_comp * 1e3, 2)}
     if name == "llama7b_qkv" and os.path.exists(TRAFFIC_FILE):
@@ -304,14 +304,15 @@ def main():
 
 
 def source_hash() -> str:
-    """Hash of the kernel sources with comments and blank lines removed, so
-    that documentation edits keep the profiled traffic figure attached."""
+    """Hash of the sources the compress kernel is built from (its file and
+    the headers it includes), with comments and blank lines removed, so that
+    documentation edits keep the profiled traffic figure attached."""
     import hashlib
     import re
     h = hashlib.sha256()
     src = os.path.join(ROOT, "activation_compression_pamm_amd", "csrc")
     for fn in sorted(os.listdir(src)):
-        if fn.endswith((".hip", ".hpp")):
+        if fn in ("pamm_compress.hip", "pamm_device.hpp", "pamm_kernels.hpp"):
             text = open(os.path.join(src, fn), encoding="utf-8").read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
             text = re.sub(r"//[^\n]*", "", text)
