@@ -249,12 +249,16 @@ def test_duplicate_generators_and_zero_and_nan_rows():
         check_wgrad(to_host(out["C"]), f_g, a_g, dY, to_host(out["dW"]))
 
 
-@pytest.mark.parametrize("n", [65536, 32768])   # 256- and 128-row blocks
-def test_gemm_tiles_degenerate_rows(n):
-    # the same degenerate cases on the GEMM-shaped kernel (bf16, 256
-    # generators): duplicate and collinear generators, a zero generator, a
-    # zero row, a NaN row
-    d, k = 128, 256
+@pytest.mark.parametrize("n,k", [
+    (65536, 256),   # 256-row blocks, one generator tile: 4 waves of 128 x 128
+    (32768, 256),   # 128-row blocks
+    (65536, 300),   # several generator tiles: 8 waves of 128 x 64, then the merge
+])
+def test_gemm_tiles_degenerate_rows(n, k):
+    # the same degenerate cases on the GEMM-shaped kernel (bf16, 256-generator
+    # tiles): duplicate and collinear generators, a zero generator, a zero
+    # row, a NaN row
+    d = 128
     X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 33, "bf16")).copy()
     X32[40] = X32[7]
     X32[41] = -4 * X32[7]
@@ -268,7 +272,7 @@ def test_gemm_tiles_degenerate_rows(n):
     s7, s100 = int(np.searchsorted(g, 7)), int(np.searchsorted(g, 100))
     gd = torch.from_numpy(g).cuda()
     for eps in (0.0, 0.2):
-        say("gemm-degenerate", eps)
+        say("gemm-degenerate", f"n={n} k={k} eps={eps}")
         C, f, a = pamm.compress(to_dev(X), gd, eps)
         torch.cuda.synchronize()
         f_g, a_g = to_host(f), to_host(a)
@@ -285,11 +289,11 @@ def test_gemm_tiles_degenerate_rows(n):
         check_compress(X, g, eps, to_host(C), f_g, a_g)
 
 
-@pytest.mark.parametrize("n", [65536, 32768])
-def test_gemm_tiles_degenerate_rows_plain_generators(n):
+@pytest.mark.parametrize("n,k", [(65536, 256), (32768, 256), (65536, 512)])
+def test_gemm_tiles_degenerate_rows_plain_generators(n, k):
     # the same rows with every generator of finite, positive norm (no zero
     # generator, no padding): the epilogue's shorter scan
-    d, k = 128, 256
+    d = 128
     X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 35, "bf16")).copy()
     X32[40] = X32[7]
     X32[41] = -4 * X32[7]
@@ -302,7 +306,7 @@ def test_gemm_tiles_degenerate_rows_plain_generators(n):
     s7 = int(np.searchsorted(g, 7))
     gd = torch.from_numpy(g).cuda()
     for eps in (0.0, 0.2):
-        say("gemm-degenerate-plain", eps)
+        say("gemm-degenerate-plain", f"n={n} k={k} eps={eps}")
         C, f, a = pamm.compress(to_dev(X), gd, eps)
         torch.cuda.synchronize()
         f_g, a_g = to_host(f), to_host(a)
