@@ -41,6 +41,9 @@
 #ifndef PAMM_COMPRESS_ROTATE
 #define PAMM_COMPRESS_ROTATE 1
 #endif
+#ifndef PAMM_RS_SKIP_IDLE_DIAG
+#define PAMM_RS_SKIP_IDLE_DIAG 1
+#endif
 
 namespace pamm {
 
@@ -377,6 +380,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
                     cf[nt] = *reinterpret_cast<const uint4*>(sc + swz<RB>(nt * 16 + (lane & 15), q));
 #pragma unroll
                 for (int g = 0; g < NDG; ++g) {
+                    if (PAMM_RS_SKIP_IDLE_DIAG && wave + g * NW >= NTL) continue;  // wave-uniform: no block left
                     const int nt = min(wave + g * NW, NTL - 1);
                     cd[g] = *reinterpret_cast<const uint4*>(sc + swz<RB>(nt * 16 + (lane & 15), q));
                 }
@@ -385,7 +389,8 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) mma16<DT>(xf[mt], cf[nt], acc[mt][nt]);
 #pragma unroll
-                for (int g = 0; g < NDG; ++g) mma16<DT>(cd[g], cd[g], dacc[g]);
+                for (int g = 0; g < NDG; ++g)
+                    if (!PAMM_RS_SKIP_IDLE_DIAG || wave + g * NW < NTL) mma16<DT>(cd[g], cd[g], dacc[g]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) xsq[mt] += sumsq16<DT>(xf[mt]);
             }
