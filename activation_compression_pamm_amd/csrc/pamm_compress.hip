@@ -44,6 +44,9 @@
 #ifndef PAMM_RS_SKIP_IDLE_DIAG
 #define PAMM_RS_SKIP_IDLE_DIAG 1
 #endif
+#ifndef PAMM_RS_SGPR_WAVE
+#define PAMM_RS_SGPR_WAVE 1
+#endif
 
 namespace pamm {
 
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     __shared__ float s_rinv[KN];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = PAMM_RS_SGPR_WAVE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;  // scalar: wave tests branch
     const int lane = tid & 63;
     // workgroup -> (row block, generator tile).  With several tiles, the
     // tiles of one row block take consecutive workgroup slots of one XCD
@@ -485,10 +488,12 @@ __device__ __forceinline__ void interleave_spread() {
 //     alpha exact for a power-of-two multiple of a generator; here no
 //     accumulation registers are left for that, so such an alpha is exact to
 //     a few fp32 ulps, and its bf16 reconstruction is still exact.)
-//   * Epilogue, through the then free stage ring: each wave writes its block
-//     of S row by row and two lanes per row scan it; the NWC column winners
-//     meet in LDS, and one thread per row merges them (lower column first,
-//     so the lowest index wins ties) and writes the result.
+//   * The MFMA takes the generator fragment as its A operand and the X
+//     fragment as B, so each lane's accumulators hold one row of S and 16 of
+//     each 32 generators.  Epilogue: each lane scans its generators of a row
+//     in registers, meets lane l^32 (the other 16 of each 32), the NWC
+//     column winners meet in LDS, and one thread per row merges them (lower
+//     column first, so the lowest index wins ties) and writes the result.
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float sumsq_dot2(const v4u32& v, float acc) {
@@ -506,11 +511,12 @@ __device__ __forceinline__ float sumsq_dot2(const v4u32& v, float acc) {
 
 // Epilogue of a Y tile (pamm_forward_compress): each wave's 32*MT x 32*NT
 // block of X W^T, plus the bias, rounded to bf16 (nearest even), goes to Y
-// through LDS in passes of 32 rows (each lane writes its 2-byte values, then
-// every lane stores whole 16-byte pieces of the staged rows; non-temporal:
-// Y is not re-read by this pass).  Rows past n and columns past d_out are not written.
-// Element i of a 32x32 result lane l is row 8*(i/4) + 4*(l/32) + i%4,
-// column l%32.
+// through LDS in passes of 32 rows (each lane writes four adjacent values at
+// a time, then every lane stores whole 16-byte pieces of the staged rows;
+// non-temporal: Y is not re-read by this pass).  Rows past n and columns past
+// d_out are not written.  The accumulators hold the product transposed (W
+// rows as the MFMA's A operand): element i of a 32x32 result lane l is row
+// l%32, column 8*(i/4) + 4*(l/32) + i%4.
 template <int MT, int NT, int NWR, int NWC>
 __device__ __forceinline__ void store_y_tile(const CompressArgs& a, const f32x16 (&acc)[MT][NT], char* ring,
                                              int64_t m0, int64_t n0, int wr, int wc, int lane, int wave) {
@@ -524,23 +530,30 @@ __device__ __forceinline__ void store_y_tile(const CompressArgs& a, const f32x16
     char* buf = ring + wave * 32 * PITCH;
     const int frow = lane & 31, fk = lane >> 5;
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.bias);
-    float bv[NT];
+    // bias of the lane's 16 columns of each 32-column block
+    float bt[NT][16];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int64_t col = n0 + wc * WN + nt * 32 + frow;
-        bv[nt] = (bias && col < a.d_out) ? bf16_to_f32(bias[col]) : 0.f;
-    }
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t col = n0 + wc * WN + nt * 32 + 8 * (i >> 2) + 4 * fk + (i & 3);
+            bt[nt][i] = (bias && col < a.d_out) ? bf16_to_f32(bias[col]) : 0.f;
+        }
     const int64_t col0 = n0 + wc * WN;
     char* Y = reinterpret_cast<char*>(a.Y);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+        // lane l holds row l%32 and columns 8*(i/4) + 4*(l/32) + i%4 of
+        // each 32-column block: four adjacent columns per 8-byte write
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 8 * (i >> 2) + 4 * fk + (i & 3);
-                *reinterpret_cast<uint16_t*>(buf + r * PITCH + (nt * 32 + frow) * 2) =
-                    (uint16_t)f32_to_bf16(acc[mt][nt][i] + bv[nt]);
+            for (int q = 0; q < 4; ++q) {
+                const int c0 = nt * 32 + 8 * q + 4 * fk;
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(acc[mt][nt][4 * q + e] + bt[nt][4 * q + e]);
+                *reinterpret_cast<uint2*>(buf + frow * PITCH + c0 * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         __syncthreads();
         const int q = lane % CH;
@@ -772,7 +785,7 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, xf[mt]), __builtin_bit_cast(bf16x8, cf[nt]), acc[mt][nt], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, cf[nt]), __builtin_bit_cast(bf16x8, xf[mt]), acc[mt][nt], 0, 0, 0);
 
     };
     // One stage position: four K steps of 16 with two fragment register sets
@@ -911,97 +924,90 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
     // tiles whose generators all have a finite, positive |c|^2 (no zero,
     // NaN or infinite norm, no padding) take the shorter scan below
     const bool plain = __syncthreads_and(plain_gen);
-    // winners: in passes of 32 rows, each wave writes its 32 x WN block of
-    // S row-major (rows padded against bank conflicts); two lanes
-    // per row then scan WN/2 generators each in increasing order (lowest
-    // index on ties, NaN never wins) and the pair is merged.  Element i of a
-    // 32x32 result lane l is row 8*(i/4) + 4*(l/32) + i%4, generator l%32.
-    // Each staged row holds the lane pair's two halves 4 floats apart from
-    // a multiple of the bank count, so the pair's reads use different banks.
-    constexpr int HW = WN / 2;         // generators scanned per lane
-    constexpr int HOFF = HW + 4;       // offset of the second half
-    constexpr int PST = WN + 8;        // floats per staged row
-    static_assert(NW * 32 * PST * (int)sizeof(float) <= 2 * TILE, "the staged S rows fit in the stage ring");
-    float* wbuf = ring + wave * 32 * PST;
-    const int sr = lane >> 1, sh = lane & 1;
-    const int jl0 = wc * WN + sh * HW;  // tile index of the lane's first generator
-    const float* rowp = wbuf + sr * PST + sh * HOFF;
-    auto stage_rows = [&](int mt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                wbuf[(8 * (i >> 2) + 4 * fk + (i & 3)) * PST + nt * 32 + frow + (nt * 32 >= HW ? HOFF - HW : 0)] =
-                    acc[mt][nt][i];
-    };
+    // winners straight from the accumulators: element i of lane l in
+    // acc[mt][nt] is S for row mt*32 + l%32 of the wave's rows and
+    // generator nt*32 + 8*(i/4) + 4*(l/32) + i%4 of its generators, so a
+    // lane scans its 16*NT generators of one row per mt in increasing
+    // order (one chain per nt, merged in nt order: lowest index on ties,
+    // NaN never wins), then meets lane l^32, which holds the others.
+    const int jb = wc * WN + 4 * fk;  // tile index of the lane's generator for nt = i = 0
+    auto gen_of = [](int nt, int i) { return nt * 32 + 8 * (i >> 2) + (i & 3); };
     auto publish = [&](int mt, float bs, int bg, float bd) __attribute__((always_inline)) {
-        const float os = shfl_xor(bs, 1);
-        const int og = shfl_xor(bg, 1);
-        const float od = shfl_xor(bd, 1);
+        const float os = shfl_xor(bs, 32);
+        const int og = shfl_xor(bg, 32);
+        const float od = shfl_xor(bd, 32);
         const bool take = os > bs || (os == bs && og < bg);
-        bs = take ? os : bs;
-        bg = take ? og : bg;
-        bd = take ? od : bd;
-        if (sh == 0) {
-            const int rloc = wr * WM + mt * 32 + sr;
-            s_ms[wc][rloc] = bs;
-            s_mg[wc][rloc] = bg;
-            s_md[wc][rloc] = bd;
+        if (fk == 0) {
+            const int rloc = wr * WM + mt * 32 + frow;
+            s_ms[wc][rloc] = take ? os : bs;
+            s_mg[wc][rloc] = take ? og : bg;
+            s_md[wc][rloc] = take ? od : bd;
         }
     };
     if (plain) {
-        // score = |S| / |c| with 1/|c| of the lane's generators in registers;
-        // only the winner's position is tracked, its S is read back after
-        float w[HW];
+        // score = |S| / |c| with 1/|c| of the lane's generators in registers
+        float w[NT][16];
 #pragma unroll
-        for (int j = 0; j < HW; j += 4) {
-            const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + jl0 + j);
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[j + e] = rv[e];
-        }
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + jb + gen_of(nt, 4 * q));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[nt][4 * q + e] = rv[e];
+            }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            stage_rows(mt);
-            float bs = -1.0f;
-            int bj = -1;
+            float cs[NT], cd[NT];
+            int cj[NT];
 #pragma unroll
-            for (int j = 0; j < HW; j += 4) {
-                const f32x4 dv = *reinterpret_cast<const f32x4*>(rowp + j);
+            for (int nt = 0; nt < NT; ++nt) {
+                cs[nt] = -1.0f;
+                cj[nt] = -1;
+                cd[nt] = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float sc = fabsf(dv[e]) * w[j + e];
-                    const bool win = sc > bs;  // false for NaN
-                    bs = win ? sc : bs;
-                    bj = win ? j + e : bj;
+                for (int i = 0; i < 16; ++i) {
+                    const float d = acc[mt][nt][i];
+                    const float sc = fabsf(d) * w[nt][i];
+                    const bool win = sc > cs[nt];  // false for NaN
+                    cs[nt] = win ? sc : cs[nt];
+                    cj[nt] = win ? gen_of(nt, i) : cj[nt];
+                    cd[nt] = win ? d : cd[nt];
                 }
             }
-            const float bd = rowp[bj < 0 ? 0 : bj];
-            publish(mt, bs, bj < 0 ? 0x7fffffff : gen0 + jl0 + bj, bj < 0 ? 0.f : bd);
+#pragma unroll
+            for (int nt = 1; nt < NT; ++nt) {
+                const bool win = cs[nt] > cs[0];
+                cs[0] = win ? cs[nt] : cs[0];
+                cj[0] = win ? cj[nt] : cj[0];
+                cd[0] = win ? cd[nt] : cd[0];
+            }
+            publish(mt, cs[0], cj[0] < 0 ? 0x7fffffff : gen0 + jb + cj[0], cd[0]);
         }
     } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            stage_rows(mt);
             float bs = -1.0f, bd = 0.f;
             int bg = 0x7fffffff;
 #pragma unroll
-            for (int j = 0; j < HW; j += 4) {
-                const f32x4 dv = *reinterpret_cast<const f32x4*>(rowp + j);
-                const int j0 = jl0 + j;
-                const f32x4 cv = *reinterpret_cast<const f32x4*>(s_cn2 + j0);
-                const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
-                const f32x4 fv = *reinterpret_cast<const f32x4*>(s_floor + j0);
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // selects, no branches: a padding generator (|c|^2 = -1)
-                    // scores -1 and never wins; |c|^2 = 0 or NaN scores 0
-                    const float sc = cv[e] > 0.f ? fabsf(dv[e]) * rv[e] : fv[e];
-                    const bool win = sc > bs;
-                    bs = win ? sc : bs;
-                    bg = win ? gen0 + j0 + e : bg;
-                    bd = win ? dv[e] : bd;
+                for (int q = 0; q < 4; ++q) {
+                    const int j0 = jb + gen_of(nt, 4 * q);
+                    const f32x4 cv = *reinterpret_cast<const f32x4*>(s_cn2 + j0);
+                    const f32x4 rv = *reinterpret_cast<const f32x4*>(s_rinv + j0);
+                    const f32x4 fv = *reinterpret_cast<const f32x4*>(s_floor + j0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // a padding generator (|c|^2 = -1) scores -1 and
+                        // never wins; |c|^2 = 0 or NaN scores 0
+                        const float d = acc[mt][nt][4 * q + e];
+                        const float sc = cv[e] > 0.f ? fabsf(d) * rv[e] : fv[e];
+                        const bool win = sc > bs;
+                        bs = win ? sc : bs;
+                        bg = win ? gen0 + j0 + e : bg;
+                        bd = win ? d : bd;
+                    }
                 }
-            }
             publish(mt, bs, bg, bd);
         }
     }
