@@ -652,6 +652,18 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
 
     if (m0 >= a.n) return;  // slot past the last row block (whole workgroup)
 
+    // |c|^2 of the tile's generators (-1 marks a padding generator of a
+    // partial tile), fetched now and put in LDS with the first stage, so the
+    // epilogue does not wait on it
+    constexpr int CNV = (BN + NTH - 1) / NTH;
+    float cn2v[CNV];
+#pragma unroll
+    for (int u = 0; u < CNV; ++u) {
+        const int r = tid + u * NTH;
+        cn2v[u] = !(FUSED && wtile) && r < ktile ? a.cn2[gen0 + r] : -1.0f;
+    }
+    int plain_gen = 1;
+
     // load i of a lane covers tile row (NTH/8)*i + tid/8 (8 lanes per row, one
     // 128-byte line per row and wave-wide load), 16-byte chunk tid%8.  Loads
     // address a wave-uniform base plus a 32-bit per-lane row offset (the
@@ -872,6 +884,17 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
             asm volatile("; no norms" ::: "memory");
         issue(0);
         stash(0, s_tile, wx);
+#pragma unroll
+        for (int u = 0; u < CNV; ++u) {
+            const int r = tid + u * NTH;
+            if (r < BN) {
+                const float v = cn2v[u];
+                s_cn2[r] = v;
+                s_rinv[r] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
+                s_floor[r] = v < 0.f ? -1.0f : 0.f;
+                plain_gen &= v > 0.f && v < INFINITY;
+            }
+        }
         issue(1);
         wait_lds();
         ring_barrier();
@@ -911,15 +934,6 @@ __global__ __launch_bounds__(64 * NWR * NWC) void compress_gemm_kernel(CompressA
 #pragma unroll
         for (int q = 0; q < 8; ++q) v += ring[r * 8 + q];
         s_xn2[r] = v;
-    }
-    int plain_gen = 1;
-    for (int r = tid; r < BN; r += NTH) {
-        // a padding generator of a partial tile is marked by |c|^2 = -1
-        const float v = r < ktile ? a.cn2[gen0 + r] : -1.0f;
-        s_cn2[r] = v;
-        s_rinv[r] = v > 0.f ? 1.0f / sqrtf(v) : 0.f;
-        s_floor[r] = v < 0.f ? -1.0f : 0.f;
-        plain_gen &= v > 0.f && v < INFINITY;
     }
     // tiles whose generators all have a finite, positive |c|^2 (no zero,
     // NaN or infinite norm, no padding) take the shorter scan below
