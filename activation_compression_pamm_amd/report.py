@@ -19,6 +19,9 @@ Derived figures per call (algorithmic work, not counter readings):
   wgrad     bytes of dY read densely (n*d_out*s) and of the kept rows only
             (kept*d_out*s), plus the dW write (4*d*d_out)
 
+For bf16 inputs the vendor GEMM of the same product (torch.mm of X and C^T,
+bf16 output, no argmax) is timed the same way, as a reference point.
+
     python -m activation_compression_pamm_amd.report [--workload W] [--k K]
         [--reps 50] [--warmup 5] [--json]
 
@@ -104,6 +107,16 @@ def run_one(name: str, k: int | None, reps: int, warmup: int) -> dict:
     log("timing wgrad")
     tw = timed(wgr, pair)
     kept = int((f >= 0).sum().item())
+    vendor = None
+    if dt == "bf16":
+        # reference point, not part of the path: the vendor GEMM (torch.mm,
+        # hipBLASLt) of the same product S = X C^T with a bf16 output and no
+        # argmax, timed the same way
+        Ct = C.t().contiguous()
+        S = torch.empty((n, kk), dtype=torch.bfloat16, device="cuda")
+        log("timing the vendor GEMM X C^T")
+        vendor = timed(lambda: torch.mm(Xd, Ct, out=S), pair)
+        del Ct, S
 
     cb = n * d * s + kk * d * s + 8 * n
     cf = 2.0 * n * d * kk
@@ -124,6 +137,10 @@ def run_one(name: str, k: int | None, reps: int, warmup: int) -> dict:
         "wgrad_dw_write_gbs": dwb / med_w / 1e3,
         "step_tokens_per_s": n / ((med_c + med_w) * 1e-6),
     }
+    if vendor is not None:
+        med_v = _pct(vendor, 50)
+        out["vendor_gemm_us"] = {"median": med_v, "p10": _pct(vendor, 10), "p90": _pct(vendor, 90)}
+        out["vendor_gemm_mfma_frac"] = cf / (med_v * 1e-6) / MFMA_PEAK[dt]
     del Xd, dYd, flush
     torch.cuda.empty_cache()
     log("done")
