@@ -41,12 +41,6 @@
 #ifndef PAMM_COMPRESS_ROTATE
 #define PAMM_COMPRESS_ROTATE 1
 #endif
-#ifndef PAMM_RS_SKIP_IDLE_DIAG
-#define PAMM_RS_SKIP_IDLE_DIAG 1
-#endif
-#ifndef PAMM_RS_SGPR_WAVE
-#define PAMM_RS_SGPR_WAVE 1
-#endif
 
 namespace pamm {
 
@@ -254,7 +248,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     __shared__ float s_rinv[KN];
 
     const int tid = threadIdx.x;
-    const int wave = PAMM_RS_SGPR_WAVE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;  // scalar: wave tests branch
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar, so tests on it are branches
     const int lane = tid & 63;
     // workgroup -> (row block, generator tile).  With several tiles, the
     // tiles of one row block take consecutive workgroup slots of one XCD
@@ -383,7 +377,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
                     cf[nt] = *reinterpret_cast<const uint4*>(sc + swz<RB>(nt * 16 + (lane & 15), q));
 #pragma unroll
                 for (int g = 0; g < NDG; ++g) {
-                    if (PAMM_RS_SKIP_IDLE_DIAG && wave + g * NW >= NTL) continue;  // wave-uniform: no block left
+                    if (wave + g * NW >= NTL) continue;  // no diagonal block left for this wave
                     const int nt = min(wave + g * NW, NTL - 1);
                     cd[g] = *reinterpret_cast<const uint4*>(sc + swz<RB>(nt * 16 + (lane & 15), q));
                 }
@@ -393,7 +387,7 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
                     for (int mt = 0; mt < MT; ++mt) mma16<DT>(xf[mt], cf[nt], acc[mt][nt]);
 #pragma unroll
                 for (int g = 0; g < NDG; ++g)
-                    if (!PAMM_RS_SKIP_IDLE_DIAG || wave + g * NW < NTL) mma16<DT>(cd[g], cd[g], dacc[g]);
+                    if (wave + g * NW < NTL) mma16<DT>(cd[g], cd[g], dacc[g]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) xsq[mt] += sumsq16<DT>(xf[mt]);
             }
