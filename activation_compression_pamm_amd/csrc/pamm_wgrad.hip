@@ -49,6 +49,10 @@
 #endif
 // with full-length chunks, generators averaging at most this many rows (n / k,
 // as if every row were kept) get paired reduction items: two chunks per item
+// the product's results go to dW as 16-byte row pieces, through LDS
+#ifndef PAMM_GEMM_VEC_STORE
+#define PAMM_GEMM_VEC_STORE 1
+#endif
 #ifndef PAMM_SR_PAIR_ROWS
 #define PAMM_SR_PAIR_ROWS 128
 #endif
@@ -604,6 +608,7 @@ struct GemmArgs {
     const int32_t* nchunks;
     float* dW;
     int64_t lddw;
+    int vec;  // dW and its leading dimension allow 16-byte stores
 };
 
 // TRANS writes dW^T [d_out x d] instead: the two operands swap places in
@@ -728,6 +733,46 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
     // for TRANS (rows in d_out, columns in d)
     const bool interior = m0 + 32 * TM <= a.d && n0 + 32 * TN <= a.d_out;
     const int64_t nrows = TRANS ? a.d_out : a.d, ncols = TRANS ? a.d : a.d_out;
+    // The wide tile (many contraction steps, k >= kWideProductK): each 32x32
+    // tile goes through this wave's slice of LDS (rows 40 floats apart: the
+    // two half-waves of a staging write fall 32 banks apart) and leaves as
+    // 16-byte pieces, 8 lanes per 128-byte row piece and 8 rows per store
+    // instruction: fewer, wider stores than the result layout's 4 bytes per
+    // lane.  A wave's LDS accesses complete in order, so the slice needs no
+    // barrier between tiles.  (With few steps, as at 7B, the product is bound
+    // by its stores and the staging delays them: the narrow tile keeps the
+    // direct stores.)
+    if constexpr (TN >= 2) if (a.vec) {
+        constexpr int TP = 40;
+        __shared__ __align__(16) float s_tile[4][32 * TP];
+        float* tb = s_tile[threadIdx.x >> 6];
+        const int sr = lane >> 3, sc = 4 * (lane & 7);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) tb[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * TP + (lane & 31)] = acc[i][j][e];
+                const int64_t row0 = TRANS ? n0 + 32 * j : m0 + 32 * i;
+                const int64_t col = (TRANS ? m0 + 32 * i : n0 + 32 * j) + sc;
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int r = 8 * it + sr;
+                    f32x4 v = *reinterpret_cast<const f32x4*>(tb + r * TP + sc);
+                    float* p = a.dW + (row0 + r) * a.lddw + col;
+                    if (interior || (row0 + r < nrows && col + 4 <= ncols)) {
+                        // non-temporal: see below
+                        if constexpr (ACC) v += *reinterpret_cast<const f32x4*>(p);
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+                    } else if (row0 + r < nrows) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (col + c < ncols) __builtin_nontemporal_store(ACC ? p[c] + v[c] : v[c], p + c);
+                    }
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -876,6 +921,7 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     GemmArgs g;
     g.AF = ws + L.off_AT; g.BF = ws + L.off_BT; g.ks_cap = L.ks_cap; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks;
     g.dW = a.dW; g.lddw = a.lddw;
+    g.vec = PAMM_GEMM_VEC_STORE && a.lddw % 4 == 0 && reinterpret_cast<uintptr_t>(a.dW) % 16 == 0;
     // With k >= kWideProductK the contraction has at least as many chunk
     // steps and the product reads its operands from L2 many times over: a
     // wider wave tile (64 x 64) halves that traffic.  With few steps the
