@@ -128,6 +128,17 @@ def _rows(t, name):
     return t.shape[0], t.shape[1], t.stride(0)
 
 
+def _empty_rows(rows, cols, dtype, device):
+    """An uninitialised [rows x cols] tensor whose rows start a multiple of
+    16 bytes apart, as the C ABI's leading-dimension rule asks: a view of a
+    buffer with padded rows when cols elements do not fill whole 16 bytes."""
+    torch = _torch()
+    per = 16 // torch.empty(0, dtype=dtype).element_size()
+    ld = (cols + per - 1) // per * per
+    buf = torch.empty((rows, ld), dtype=dtype, device=device)
+    return buf if ld == cols else buf[:, :cols]
+
+
 def _on_gpu(where, **tensors):
     """Every tensor argument must live on one GPU: the kernels read and write
     them in place."""
@@ -246,7 +257,9 @@ def forward_compress(X, W, gen_idx, eps: float, *, bias=None, Y=None, C=None, f=
     """The projection Y = X W^T (+ bias) and the compression of X in one pass
     over X (bf16 only).  X [n x d], W [d_out x d] (the layout of a linear
     layer's weight), bias [d_out] or None, gen_idx int32 [k] on the device.
-    Returns (Y [n x d_out] bf16, C [k x d], f [n] int32, alpha [n] fp32)."""
+    Returns (Y [n x d_out] bf16, C [k x d], f [n] int32, alpha [n] fp32).
+    A Y allocated here has its rows padded to a multiple of 16 bytes (the
+    returned tensor is a view of the exact shape)."""
     torch = _torch()
     n, d, ldx = _rows(X, "X")
     dt = _dtype_code(X)
@@ -267,7 +280,7 @@ def forward_compress(X, W, gen_idx, eps: float, *, bias=None, Y=None, C=None, f=
     _on_gpu("forward_compress", X=X, W=W, bias=bias, Y=Y, C=C, f=f, alpha=alpha, workspace=workspace)
     gen_idx = gen_idx.to(device=X.device, dtype=torch.int32).contiguous()
     if Y is None:
-        Y = torch.empty((n, d_out), dtype=X.dtype, device=X.device)
+        Y = _empty_rows(n, d_out, X.dtype, X.device)
     _, _, ldy = _rows(Y, "Y")
     if C is None:
         C = torch.empty((k, d), dtype=X.dtype, device=X.device)
@@ -289,7 +302,9 @@ def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: 
     """Approximate weight gradient dW = C^T B~ [d x d_out] (fp32) from the
     compressed triple and the output gradient dY [n x d_out].  With
     transpose_out the result is dW^T [d_out x d], the layout of the weight
-    gradient of a layer Y = X W^T."""
+    gradient of a layer Y = X W^T.  A dW allocated here has its rows padded
+    to a multiple of 16 bytes (the returned tensor is a view of the exact
+    shape)."""
     torch = _torch()
     n, d_out, lddy = _rows(dY, "dY")
     dt = _dtype_code(dY)
@@ -305,7 +320,7 @@ def wgrad(C, f, alpha, dY, *, dW=None, accumulate: bool = False, transpose_out: 
         raise ValueError(f"dW must be float32 of shape {shape}, got {tuple(dW.shape)} {dW.dtype}")
     _on_gpu("wgrad", C=C, f=f, alpha=alpha, dY=dY, dW=dW, workspace=workspace)
     if dW is None:
-        dW = torch.empty(shape, dtype=torch.float32, device=dY.device)
+        dW = _empty_rows(shape[0], shape[1], torch.float32, dY.device)
     _, _, lddw = _rows(dW, "dW")
     ws = _workspace(wgrad_workspace_size(n, k, d, d_out, dt), dY.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -343,7 +358,9 @@ def wgrad_noalloc(C, f, alpha, dY, dW, *, accumulate: bool = False, transpose_ou
 
 
 def decompress(C, f, alpha, *, out=None, stream=None):
-    """Reconstruction X~_i = alpha_i C_f(i) (zero rows where f = -1)."""
+    """Reconstruction X~_i = alpha_i C_f(i) (zero rows where f = -1).  An out
+    allocated here has its rows padded to a multiple of 16 bytes (the returned
+    tensor is a view of the exact shape)."""
     torch = _torch()
     if C.dim() != 2:
         raise ValueError(f"decompress: C must be 2-D [k x d], got shape {tuple(C.shape)}")
@@ -357,7 +374,7 @@ def decompress(C, f, alpha, *, out=None, stream=None):
         raise ValueError(f"out must be {C.dtype} of shape {(n, d)}, got {tuple(out.shape)} {out.dtype}")
     _on_gpu("decompress", C=C, f=f, alpha=alpha, out=out)
     if out is None:
-        out = torch.empty((n, d), dtype=C.dtype, device=f.device)
+        out = _empty_rows(n, d, C.dtype, f.device)
     _, _, ldxt = _rows(out, "out")
     st = load_library().pamm_decompress(_ptr(C), _ptr(f), _ptr(alpha), n, k, d, dt, _ptr(out), ldxt,
                                         _stream_ptr(stream))

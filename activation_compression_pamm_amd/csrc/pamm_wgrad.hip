@@ -49,10 +49,6 @@
 #endif
 // with full-length chunks, generators averaging at most this many rows (n / k,
 // as if every row were kept) get paired reduction items: two chunks per item
-// the product's results go to dW as 16-byte row pieces, through LDS
-#ifndef PAMM_GEMM_VEC_STORE
-#define PAMM_GEMM_VEC_STORE 1
-#endif
 #ifndef PAMM_SR_PAIR_ROWS
 #define PAMM_SR_PAIR_ROWS 128
 #endif
@@ -608,7 +604,6 @@ struct GemmArgs {
     const int32_t* nchunks;
     float* dW;
     int64_t lddw;
-    int vec;  // dW and its leading dimension allow 16-byte stores
 };
 
 // TRANS writes dW^T [d_out x d] instead: the two operands swap places in
@@ -739,10 +734,11 @@ __global__ __launch_bounds__(256) void gen_gemm_kernel(GemmArgs a) {
     // 16-byte pieces, 8 lanes per 128-byte row piece and 8 rows per store
     // instruction: fewer, wider stores than the result layout's 4 bytes per
     // lane.  A wave's LDS accesses complete in order, so the slice needs no
-    // barrier between tiles.  (With few steps, as at 7B, the product is bound
-    // by its stores and the staging delays them: the narrow tile keeps the
-    // direct stores.)
-    if constexpr (TN >= 2) if (a.vec) {
+    // barrier between tiles (dW and its leading dimension are 16-byte
+    // aligned, which the interface requires).  With few steps, as at 7B, the
+    // product is bound by its stores and the staging delays them: the narrow
+    // tile keeps the direct stores.
+    if constexpr (TN >= 2) {
         constexpr int TP = 40;
         __shared__ __align__(16) float s_tile[4][32 * TP];
         float* tb = s_tile[threadIdx.x >> 6];
@@ -921,7 +917,6 @@ static hipError_t wgrad_impl(const WgradArgs& a, hipStream_t st) {
     GemmArgs g;
     g.AF = ws + L.off_AT; g.BF = ws + L.off_BT; g.ks_cap = L.ks_cap; g.d = a.d; g.d_out = a.d_out; g.nchunks = nchunks;
     g.dW = a.dW; g.lddw = a.lddw;
-    g.vec = PAMM_GEMM_VEC_STORE && a.lddw % 4 == 0 && reinterpret_cast<uintptr_t>(a.dW) % 16 == 0;
     // With k >= kWideProductK the contraction has at least as many chunk
     // steps and the product reads its operands from L2 many times over: a
     // wider wave tile (64 x 64) halves that traffic.  With few steps the

@@ -379,6 +379,44 @@ def test_accumulate_and_strided_views(dtype, d, dout):
     assert np.all(orc.to_f64(xt[:, d:]) == 7.0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_default_outputs_with_ragged_rows(dtype):
+    # widths whose rows do not fill whole 16 bytes: outputs the binding
+    # allocates get padded rows (the leading-dimension rule of the C ABI) and
+    # hold the same bits as outputs the caller supplies; k = 300 takes the
+    # wide product tile, whose last 16-byte piece of a row is partly outside
+    n, d, dout, k = 3000, 123, 157, 300
+    ldx = (d + 7) // 8 * 8 + 8
+    lddy = (dout + 7) // 8 * 8 + 8
+    Xbig = synth.clustered_activations(n, ldx, 8, seed=81, dtype=dtype)
+    dYbig = synth.gradients(n, lddy, seed=82, dtype=dtype)
+    Xd, dYd = to_dev(Xbig)[:, :d], to_dev(dYbig)[:, :dout]
+    g = pamm.sample_generators(n, k, 83).cuda()
+    say("default outputs", dtype, f"n={n} d={d} d_out={dout} k={k}")
+    C, f, a = pamm.compress(Xd, g, 0.1)
+    dW = pamm.wgrad(C, f, a, dYd)
+    given = torch.full((d, dout + 3), 5.0, device="cuda")
+    pamm.wgrad(C, f, a, dYd, dW=given[:, :dout])
+    dWt = pamm.wgrad(C, f, a, dYd, transpose_out=True)
+    xt = pamm.decompress(C, f, a)
+    xt2 = pamm.decompress(C, f, a, out=torch.empty((n, ldx), dtype=C.dtype, device="cuda")[:, :d])
+    torch.cuda.synchronize()
+    assert dW.shape == (d, dout) and dWt.shape == (dout, d) and xt.shape == (n, d)
+    assert torch.equal(dW, given[:, :dout]) and torch.equal(dWt, dW.t()) and torch.equal(xt, xt2)
+    assert torch.all(given[:, dout:] == 5.0)
+    ref = orc.wgrad(to_host(C), to_host(f), to_host(a), np.ascontiguousarray(dYbig[:, :dout]))
+    assert rel(to_host(dW), ref) < 1e-4
+    if dtype == "bf16":
+        dy = 150                      # Y rows of 300 bytes
+        Wbig = synth.random_matrix(dy, ldx, 84, "bf16")
+        Wd = to_dev(Wbig)[:, :d]
+        Y = pamm.forward_compress(Xd, Wd, g, 0.1)[0]
+        Yg = torch.empty((n, dy + 2), dtype=torch.bfloat16, device="cuda")[:, :dy]
+        pamm.forward_compress(Xd, Wd, g, 0.1, Y=Yg)
+        torch.cuda.synchronize()
+        assert Y.shape == (n, dy) and torch.equal(Y, Yg)
+
+
 def test_deterministic_bitwise():
     X, dY, p = synth.make_config("gpt2_small_qkv")
     g = pamm.sample_generators(p["n"], p["k"], 9).numpy()
