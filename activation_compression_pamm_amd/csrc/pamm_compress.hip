@@ -11,7 +11,7 @@
 //   * X and C (= rows gen_idx of X) are fetched from HBM into VGPRs as full
 //     128-byte lines (8 lanes per row, the pattern HBM serves fastest; rows
 //     fetched in MFMA-fragment order, 64 bytes per row per instruction, ran
-//     at about 70% of that rate), PD stages ahead in a register ring, then
+//     at about 89% of that rate), PD stages ahead in a register ring, then
 //     written to a double-buffered LDS tile, XOR-swizzled so MFMA fragment
 //     reads avoid bank clashes.  Every load lands in registers, so the
 //     compiler tracks every wait; each trip issues the same loads.
