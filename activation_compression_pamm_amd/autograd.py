@@ -68,6 +68,8 @@ class PammLinearFunction(torch.autograd.Function):
             dW = wgrad(C, f, alpha, dY2, transpose_out=True)
             if dW.dtype != W.dtype:
                 dW = dW.to(W.dtype)
+            if not dW.is_contiguous():  # rows padded to 16 bytes when in_features is ragged
+                dW = dW.contiguous()
         if ctx.has_bias and ctx.needs_input_grad[2]:
             db = dY2.float().sum(0).to(dY2.dtype)
         return dX, dW, db, None, None, None
