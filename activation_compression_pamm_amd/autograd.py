@@ -21,9 +21,20 @@ from __future__ import annotations
 
 import torch
 
-from . import MAX_K, compress, sample_generators, wgrad
+from . import MAX_K, _empty_rows, compress, sample_generators, wgrad
 
 __all__ = ["PammLinearFunction", "PammLinear", "generators_for"]
+
+
+def _aligned_rows(t2):
+    """t2 [rows x cols] itself when its rows are contiguous and start a
+    multiple of 16 bytes apart (what the library's calls ask of their
+    inputs), else a copy into a buffer with rows padded to 16 bytes."""
+    if t2.stride(1) == 1 and (t2.stride(0) * t2.element_size()) % 16 == 0 and t2.data_ptr() % 16 == 0:
+        return t2
+    out = _empty_rows(t2.shape[0], t2.shape[1], t2.dtype, t2.device)
+    out.copy_(t2)
+    return out
 
 
 def generators_for(n: int, ratio: int) -> int:
@@ -43,13 +54,14 @@ class PammLinearFunction(torch.autograd.Function):
         X2 = X.reshape(-1, d)
         if not X2.is_contiguous():
             X2 = X2.contiguous()
+        Xc = _aligned_rows(X2)   # X2 itself unless d leaves its rows off 16 bytes
         # generators: drawn on the host into page-locked memory and uploaded
         # asynchronously ahead of the projection, so the upload neither syncs
         # the stream nor waits behind the GEMM (torch keeps the host buffer
         # alive until the copy has run)
         gen = sample_generators(X2.shape[0], k, seed, pin=True).to(X.device, non_blocking=True)
         Y = torch.nn.functional.linear(X2, W, b)
-        C, f, alpha = compress(X2, gen, eps)
+        C, f, alpha = compress(Xc, gen, eps)
         ctx.save_for_backward(C, f, alpha, W)
         ctx.has_bias = b is not None
         ctx.x_shape = X.shape
@@ -65,7 +77,7 @@ class PammLinearFunction(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             dX = (dY2 @ W).reshape(ctx.x_shape)
         if ctx.needs_input_grad[1]:
-            dW = wgrad(C, f, alpha, dY2, transpose_out=True)
+            dW = wgrad(C, f, alpha, _aligned_rows(dY2), transpose_out=True)
             if dW.dtype != W.dtype:
                 dW = dW.to(W.dtype)
             if not dW.is_contiguous():  # rows padded to 16 bytes when in_features is ragged

@@ -48,10 +48,11 @@ def test_transposed_output_is_the_transpose(dtype, k):
     assert torch.equal(big[:, :8], before[:, :8]) and torch.equal(big[:, 8 + d:], before[:, 8 + d:])
 
 
+@pytest.mark.parametrize("d,dout", [(256, 384), (123, 157)])   # 123, 157: rows off 16 bytes, padded inside
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_pamm_linear_outputs_and_gradients(dtype):
+def test_pamm_linear_outputs_and_gradients(dtype, d, dout):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    Bt, S, d, dout, ratio, eps = 4, 512, 256, 384, 16, 0.1
+    Bt, S, ratio, eps = 4, 512, 16, 0.1
     n = Bt * S
     say("PammLinear", dtype, f"X [{Bt}x{S}x{d}] -> [{dout}], ratio={ratio} eps={eps}")
     torch.manual_seed(0)
@@ -77,8 +78,11 @@ def test_pamm_linear_outputs_and_gradients(dtype):
     # the weight gradient: the oracle's wgrad fed the same compressed triple
     k = generators_for(n, ratio)
     g = pamm.sample_generators(n, k, seed)
-    C, f, a = pamm.compress(X.detach().reshape(n, d), g.cuda(), eps)
+    Xp = torch.zeros((n, (d + 7) // 8 * 8), dtype=tdt, device="cuda")   # rows 16-byte multiples
+    Xp[:, :d] = X.detach().reshape(n, d)
+    C, f, a = pamm.compress(Xp[:, :d], g.cuda(), eps)
     dW_o = orc.wgrad(to_host(C), to_host(f), to_host(a), to_host(dY))
+    assert layer.weight.grad.is_contiguous()
     assert rel(layer.weight.grad.double().cpu().numpy().T, dW_o) <= TOL[dtype]
     # what the backward pass keeps: the triple and W, never X
     assert sorted(tuple(t.shape) for t in saved) == sorted([(k, d), (n,), (n,), (dout, d)])
