@@ -1209,10 +1209,19 @@ static bool gemm_pays_cfg(const CompressArgs& a, int ntiles) { return gemm_pays<
 
 template <int DT>
 static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, hipStream_t st) {
+    // Few rows (fewer 128-row blocks than compute units, e.g. GPT-2's 8192
+    // tokens) and one small generator tile: 2-wave workgroups of 32 rows put
+    // four times as many workgroups in flight, at the price of a generator
+    // tile read per 32 rows instead of per 128 (2-8 KB per stage at k <= 64).
+    // GPT-2 and the tiny fp32 case: compress ~20% faster.
+    const bool few_rows = ntiles == 1 && (a.n + 127) / 128 < (int64_t)a.num_cus;
     switch (kn) {
-        case 16: return launch_compress_rs<DT, PAMM_COMPRESS_RS16>(a, ntiles, st);
-        case 32: return launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
-        case 64: return launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
+        case 16: return few_rows ? launch_compress_rs<DT, 16, 2, 16, 4, 128>(a, ntiles, st)
+                                 : launch_compress_rs<DT, PAMM_COMPRESS_RS16>(a, ntiles, st);
+        case 32: return few_rows ? launch_compress_rs<DT, 16, 2, 32, 4, 128>(a, ntiles, st)
+                                 : launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
+        case 64: return few_rows ? launch_compress_rs<DT, 16, 2, 64, 4, 128>(a, ntiles, st)
+                                 : launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
         case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
         default:
             if constexpr (DT == DT_BF16) {
