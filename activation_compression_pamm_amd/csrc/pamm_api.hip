@@ -82,7 +82,7 @@ const char* pamm_status_string(int status) {
         case PAMM_ERR_UNSUPPORTED: return "unsupported request";
         case PAMM_ERR_HIP: return "HIP runtime error at launch";
         case PAMM_ERR_VALUE: return "a scalar argument is out of range";
-        case PAMM_ERR_TOO_LARGE: return "the problem needs more workspace than the fixed no-allocation scratch array holds";
+        case PAMM_ERR_TOO_LARGE: return "the problem needs more memory than is available (the fixed no-allocation scratch array, or host memory for sampling)";
         default: return "unknown status";
     }
 }
@@ -92,13 +92,21 @@ int pamm_sample_generators(int64_t n, int64_t k, uint64_t seed, int32_t* gen_idx
     if (k == 0) return PAMM_OK;
     if (!gen_idx_host) return PAMM_ERR_NULL;
     // Floyd: for j = n-k .. n-1 draw t in [0, j]; keep t if new, else keep j.
-    std::vector<uint8_t> taken((size_t)n, 0);
+    // The taken set is a bitmap of n bits; an allocation failure is a status,
+    // not an exception that would cross the C interface.
+    std::vector<uint64_t> taken;
+    try {
+        taken.assign((size_t)((n + 63) / 64), 0);
+    } catch (...) {
+        return PAMM_ERR_TOO_LARGE;
+    }
     SplitMix64 rng{seed};
     int64_t m = 0;
     for (int64_t j = n - k; j < n; ++j) {
         const int64_t t = (int64_t)rng.below((uint64_t)j + 1);
-        const int64_t pick = taken[(size_t)t] ? j : t;
-        taken[(size_t)pick] = 1;
+        const bool seen = (taken[(size_t)t >> 6] >> (t & 63)) & 1u;
+        const int64_t pick = seen ? j : t;
+        taken[(size_t)pick >> 6] |= 1ull << (pick & 63);
         gen_idx_host[m++] = (int32_t)pick;
     }
     std::sort(gen_idx_host, gen_idx_host + k);

@@ -58,7 +58,8 @@ typedef enum {
     PAMM_ERR_UNSUPPORTED = 6, /* valid request this build does not implement    */
     PAMM_ERR_HIP = 7,         /* the HIP runtime reported an error at launch    */
     PAMM_ERR_VALUE = 8,       /* a scalar argument is out of range (e.g. eps)   */
-    PAMM_ERR_TOO_LARGE = 9    /* needs more than the no-allocation scratch array */
+    PAMM_ERR_TOO_LARGE = 9    /* needs more memory than available: the no-allocation
+                                 scratch array, or host memory for sampling          */
 } pamm_status_t;
 
 /* PAMM_ABI_VERSION of the loaded library. */
@@ -77,8 +78,10 @@ const char *pamm_status_string(int status);
  * algorithm (j = n-k .. n-1: draw t uniform in [0, j], take t unless already
  * taken, else j) driven by SplitMix64 seeded with `seed`; a uniform integer in
  * [0, m) is the high 64 bits of the 128-bit product of a SplitMix64 output
- * and m.  Errors: PAMM_ERR_SHAPE if k < 0, k > n or n >= 2^31;
- * PAMM_ERR_NULL if k > 0 and gen_idx_host is NULL.
+ * and m.  Host memory: n bits for the set of rows taken.  Errors:
+ * PAMM_ERR_SHAPE if k < 0, k > n or n >= 2^31; PAMM_ERR_NULL if k > 0 and
+ * gen_idx_host is NULL; PAMM_ERR_TOO_LARGE if those n bits cannot be
+ * allocated.
  */
 int pamm_sample_generators(int64_t n, int64_t k, uint64_t seed, int32_t *gen_idx_host);
 

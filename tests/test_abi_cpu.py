@@ -49,7 +49,8 @@ def test_version_and_status_strings(lib):
     assert lib.pamm_status_string(12345) == b"unknown status"
 
 
-@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (100, 100), (32768, 64), (131072, 256), (1000, 0), (2048, 1024)])
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (100, 100), (32768, 64), (131072, 256), (1000, 0), (2048, 1024),
+                                 (64, 17), (65, 65), (2**31 - 1, 5)])  # bitmap word edges, the largest n
 def test_sampler_matches_oracle(n, k):
     for seed in (0, 1, 2002, 2**63 + 5):
         lib_idx = pamm.sample_generators(n, k, seed).numpy()
@@ -156,7 +157,7 @@ def test_wgrad_noalloc_validation(lib):
     big = dict(n=65536, k=4096, d=4096, dout=12288, lddy=12288, lddw=12288)
     assert lib.pamm_wgrad_workspace_size(65536, 4096, 4096, 12288, 1) > pamm.NOALLOC_SCRATCH_BYTES
     assert call(**big) == ETOOLARGE
-    assert lib.pamm_status_string(ETOOLARGE).startswith(b"the problem needs more workspace")
+    assert lib.pamm_status_string(ETOOLARGE).startswith(b"the problem needs more memory")
     # the largest workloads of the benchmark configurations fit
     for n, k, d, dout in ((32768, 1024, 2048, 6144), (131072, 256, 4096, 6144), (32768, 64, 4096, 12288)):
         assert lib.pamm_wgrad_workspace_size(n, k, d, dout, 1) <= pamm.NOALLOC_SCRATCH_BYTES
