@@ -19,6 +19,12 @@ int per16(int dtype) { return 16 / elem_size(dtype); }
 bool dtype_ok(int dtype) { return dtype == PAMM_F32 || dtype == PAMM_BF16; }
 
 constexpr int64_t kMaxRows = 2147483647LL;
+// Largest span of a matrix, (rows - 1) * ld + row length, in elements: far
+// beyond any device's memory, and small enough that no byte offset overflows.
+constexpr int64_t kMaxSpan = (int64_t)1 << 40;
+bool span_ok(int64_t rows, int64_t ld, int64_t len) {
+    return rows <= 0 || (ld <= kMaxSpan && rows - 1 <= (kMaxSpan - len) / ld);
+}
 
 // SplitMix64 generator (Steele, Lea, Flood 2014): a Weyl sequence with
 // increment 0x9E3779B97F4A7C15 passed through a two-round multiply/xorshift
@@ -56,6 +62,8 @@ int wgrad_check(const void* C, const int32_t* f, const float* alpha, int64_t n, 
     if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
     if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || d_out < 1 ||
         d_out > kMaxRows || (n > 0 && lddy < d_out) || lddw < (transpose_out ? d : d_out))
+        return PAMM_ERR_SHAPE;
+    if (!span_ok(n, lddy, d_out) || !span_ok(transpose_out ? d_out : d, lddw, transpose_out ? d : d_out))
         return PAMM_ERR_SHAPE;
     if (!dW || (n > 0 && (!f || !alpha || !dY)) || (k > 0 && !C)) return PAMM_ERR_NULL;
     if (!aligned(dW, 16) || lddw % 4 != 0) return PAMM_ERR_ALIGN;
@@ -152,7 +160,8 @@ size_t pamm_compress_workspace_size(int64_t n, int64_t d, int64_t k, int dtype) 
 int pamm_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int dtype, const int32_t* gen_idx, int64_t k,
                   float eps, void* C, int32_t* f, float* alpha, void* ws, size_t ws_bytes, void* stream) {
     if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
-    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || ldx < d)
+    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || ldx < d ||
+        !span_ok(n, ldx, d))
         return PAMM_ERR_SHAPE;
     if (!(eps >= 0.0f) || isinf(eps)) return PAMM_ERR_VALUE;
     if (n == 0) return PAMM_OK;
@@ -225,7 +234,8 @@ int pamm_forward_compress(const void* X, int64_t n, int64_t d, int64_t ldx, int 
                           float eps, void* C, int32_t* f, float* alpha, void* ws, size_t ws_bytes, void* stream) {
     if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
     if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || ldx < d ||
-        d_out < 1 || d_out > kMaxRows || ldw < d || ldy < d_out)
+        d_out < 1 || d_out > kMaxRows || ldw < d || ldy < d_out || !span_ok(n, ldx, d) || !span_ok(d_out, ldw, d) ||
+        !span_ok(n, ldy, d_out))
         return PAMM_ERR_SHAPE;
     if (!(eps >= 0.0f) || isinf(eps)) return PAMM_ERR_VALUE;
     if (dtype != PAMM_BF16) return PAMM_ERR_UNSUPPORTED;
@@ -314,7 +324,8 @@ int pamm_wgrad(const void* C, const int32_t* f, const float* alpha, int64_t n, i
 int pamm_decompress(const void* C, const int32_t* f, const float* alpha, int64_t n, int64_t k, int64_t d, int dtype,
                     void* Xt, int64_t ldxt, void* stream) {
     if (!dtype_ok(dtype)) return PAMM_ERR_DTYPE;
-    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || ldxt < d)
+    if (n < 0 || n > kMaxRows || k < 0 || k > n || k > PAMM_MAX_K || d < 1 || d > kMaxRows || ldxt < d ||
+        !span_ok(n, ldxt, d))
         return PAMM_ERR_SHAPE;
     if (n == 0) return PAMM_OK;
     if (!f || !alpha || !Xt || (k > 0 && !C)) return PAMM_ERR_NULL;

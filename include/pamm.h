@@ -30,7 +30,9 @@
  *   - Every call returns a pamm_status_t.  Arguments are fully validated
  *     before anything is enqueued; on any error nothing is launched and no
  *     output is written.  No C++ exception crosses this interface.
- *   - Sizes: 0 <= k <= n < 2^31, k <= PAMM_MAX_K, d >= 1, d_out >= 1.
+ *   - Sizes: 0 <= k <= n < 2^31, k <= PAMM_MAX_K, d >= 1, d_out >= 1, and
+ *     every matrix spans at most 2^40 elements ((rows - 1) * ld + row
+ *     length); otherwise PAMM_ERR_SHAPE.
  */
 #ifndef PAMM_H
 #define PAMM_H

@@ -94,6 +94,9 @@ def test_compress_validation(lib):
     assert call_compress(lib, ldx=31) == ESHAPE
     assert call_compress(lib, d=0, ldx=0) == ESHAPE
     assert call_compress(lib, n=10000, k=5000) == ESHAPE  # k above PAMM_MAX_K
+    # a matrix spanning more than 2^40 elements
+    assert call_compress(lib, n=1 << 21, ldx=1 << 20) == ESHAPE
+    assert call_compress(lib, n=1, ldx=1 << 41) == ESHAPE
     assert call_compress(lib, eps=-0.5) == EVALUE
     assert call_compress(lib, eps=float("nan")) == EVALUE
     assert call_compress(lib, eps=float("inf")) == EVALUE
@@ -127,6 +130,8 @@ def test_wgrad_validation(lib):
     assert call_wgrad(lib, lddy=40) == ESHAPE
     assert call_wgrad(lib, lddw=40) == ESHAPE
     assert call_wgrad(lib, dout=0, lddy=0, lddw=0) == ESHAPE
+    assert call_wgrad(lib, n=1 << 21, lddy=1 << 20) == ESHAPE     # dY spans more than 2^40 elements
+    assert call_wgrad(lib, d=1 << 21, lddw=1 << 20) == ESHAPE     # so does dW
     assert call_wgrad(lib, dW=None) == ENULL
     assert call_wgrad(lib, dY=None) == ENULL
     assert call_wgrad(lib, C=None) == ENULL
@@ -181,6 +186,7 @@ def test_forward_compress_validation(lib):
     assert call(ldw=16) == ESHAPE
     assert call(ldy=40) == ESHAPE
     assert call(dout=0, ldy=0) == ESHAPE
+    assert call(n=1 << 21, ldx=1 << 20, ldy=1 << 20) == ESHAPE     # X and Y span more than 2^40 elements
     assert call(k=65) == ESHAPE
     assert call(eps=-0.5) == EVALUE
     assert call(W=None) == ENULL
@@ -205,6 +211,7 @@ def test_decompress_validation(lib):
     assert call(dt=3) == EDTYPE
     assert call(k=65) == ESHAPE
     assert call(ld=16) == ESHAPE
+    assert call(n=1 << 21, ld=1 << 20) == ESHAPE
     assert call(Xt=None) == ENULL
     assert call(Xt=FAKE + 8) == EALIGN
     assert call(n=0, k=0, C=None, f=None, a=None, Xt=None) == OK
