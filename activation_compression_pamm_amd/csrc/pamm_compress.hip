@@ -23,7 +23,9 @@
 //   * |c_j|^2 comes from extra MFMAs of the C fragments with themselves, the
 //     same arithmetic as a dot product, so a row that is a power-of-two
 //     multiple of a generator gets an exact alpha.
-//   * |x_i|^2 is summed in fp32 from the X fragments the wave already holds.
+//   * |x_i|^2 likewise: bf16 takes the diagonal of MFMAs of the wave's X
+//     fragments with themselves (the matrix cores idle most of the time at
+//     small k, the VALU does not); fp32 sums squares on the VALU.
 //   * Epilogue: per-row argmax of |S_ij| / |c_j| across the 16 lanes of a row
 //     (lowest index on ties, NaN never wins), cosine test against eps, alpha =
 //     S_if / |c_f|^2.
@@ -334,9 +336,17 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
         for (int nt = 0; nt < NTL; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < NDG; ++g) dacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // |x|^2: bf16 takes the diagonal of an MFMA of the X fragments with
+    // themselves (the matrix cores are mostly idle here, the VALU is not);
+    // fp32 sums squares on the VALU
+    constexpr bool XMFMA = DT == DT_BF16;
     float xsq[MT];
+    f32x4 xacc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xsq[mt] = 0.f;
+    for (int mt = 0; mt < MT; ++mt) {
+        xsq[mt] = 0.f;
+        xacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     static_for<0, PD>([&](auto uc) { issue(decltype(uc)::value, uc); });
 
@@ -389,7 +399,10 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
                 for (int g = 0; g < NDG; ++g)
                     if (wave + g * NW < NTL) mma16<DT>(cd[g], cd[g], dacc[g]);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xsq[mt] += sumsq16<DT>(xf[mt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    if constexpr (XMFMA) mma16<DT>(xf[mt], xf[mt], xacc[mt]);
+                    else xsq[mt] += sumsq16<DT>(xf[mt]);
+                }
             }
         });
     }
@@ -408,9 +421,17 @@ __global__ __launch_bounds__(64 * NW) void compress_rs_kernel(CompressArgs a) {
     float xn2r[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        float v = xsq[mt];
-        v += shfl_xor(v, 16);
-        v += shfl_xor(v, 32);
+        float v;
+        if constexpr (XMFMA) {
+            // row r of the block sits at element r%4 of lane 16*(r/4) + r
+            const int r = lane & 15, e = r & 3;
+            const float own = e == 0 ? xacc[mt][0] : e == 1 ? xacc[mt][1] : e == 2 ? xacc[mt][2] : xacc[mt][3];
+            v = __shfl(own, 16 * (r >> 2) + r, 64);
+        } else {
+            v = xsq[mt];
+            v += shfl_xor(v, 16);
+            v += shfl_xor(v, 32);
+        }
         xn2r[mt] = v;
     }
     __syncthreads();
