@@ -107,6 +107,19 @@ def test_sort_block_edges_and_largest_k(n, d, dout, k):
     full_case(X, dY, g, 0.05, "sort-path")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("k", [33, 64, 100])
+def test_full_row_blocks_with_a_ragged_stage(dtype, k):
+    # enough rows for the 8-wave small-k compress (a 128-row block per
+    # compute unit) and a row length that ends in a partial stage, which
+    # the rotated stage order places in the middle of most workgroups' walks
+    n, d, dout = 40000, 200, 96
+    X = synth.clustered_activations(n, d, 48, seed=n + k, dtype=dtype)
+    dY = synth.gradients(n, dout, seed=n + dout + k, dtype=dtype)
+    g = pamm.sample_generators(n, k, seed=k + 5).numpy()
+    full_case(X, dY, g, 0.1, f"ragged-stage-{dtype}")
+
+
 @pytest.mark.parametrize("n,d,dout,k,dtype", [
     (20000, 64, 1024, 512, "f32"),
     (30001, 72, 1544, 300, "bf16"),   # ragged rows and output columns
