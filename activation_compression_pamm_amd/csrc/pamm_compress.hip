@@ -1174,20 +1174,25 @@ static hipError_t launch_compress_gemm(const CompressArgs& a, int ntiles, hipStr
 
 // Tile shapes per generator-tile width: rows per wave, waves, generators,
 // register prefetch depth (stages), bytes of each row per stage.  The
-// 256-generator tile prefetches two stages: with four, its accumulators,
-// fragments and ring exceed the 256 registers a wave of a 512-thread
-// workgroup may hold, and the spills cost twice the time.
+// 8-wave tiles prefetch two stages: measured against four (same outputs),
+// two took 0.5-1.5 us less at 7B and on the 1B sweep, and six or eight took
+// more.  The 256-generator tile could not hold four anyway: its
+// accumulators, fragments and ring would exceed the 256 registers a wave of
+// a 512-thread workgroup may hold.  The 2-wave tiles for few rows keep four.
+#ifndef PAMM_COMPRESS_FEW_PD
+#define PAMM_COMPRESS_FEW_PD 4
+#endif
 #ifndef PAMM_COMPRESS_RS16
-#define PAMM_COMPRESS_RS16 16, 8, 16, 4, 128
+#define PAMM_COMPRESS_RS16 16, 8, 16, 2, 128
 #endif
 #ifndef PAMM_COMPRESS_RS32
-#define PAMM_COMPRESS_RS32 16, 8, 32, 4, 128
+#define PAMM_COMPRESS_RS32 16, 8, 32, 2, 128
 #endif
 #ifndef PAMM_COMPRESS_RS64
-#define PAMM_COMPRESS_RS64 16, 8, 64, 4, 128
+#define PAMM_COMPRESS_RS64 16, 8, 64, 2, 128
 #endif
 #ifndef PAMM_COMPRESS_RS128
-#define PAMM_COMPRESS_RS128 16, 8, 128, 4, 128
+#define PAMM_COMPRESS_RS128 16, 8, 128, 2, 128
 #endif
 #ifndef PAMM_COMPRESS_RS256
 #define PAMM_COMPRESS_RS256 16, 8, 256, 2, 128
@@ -1236,12 +1241,13 @@ static hipError_t compress_dispatch(const CompressArgs& a, int kn, int ntiles, h
     // tile read per 32 rows instead of per 128 (2-8 KB per stage at k <= 64).
     // GPT-2 and the tiny fp32 case: compress ~20% faster.
     const bool few_rows = ntiles == 1 && (a.n + 127) / 128 < (int64_t)a.num_cus;
+    constexpr int FP = PAMM_COMPRESS_FEW_PD;
     switch (kn) {
-        case 16: return few_rows ? launch_compress_rs<DT, 16, 2, 16, 4, 128>(a, ntiles, st)
+        case 16: return few_rows ? launch_compress_rs<DT, 16, 2, 16, FP, 128>(a, ntiles, st)
                                  : launch_compress_rs<DT, PAMM_COMPRESS_RS16>(a, ntiles, st);
-        case 32: return few_rows ? launch_compress_rs<DT, 16, 2, 32, 4, 128>(a, ntiles, st)
+        case 32: return few_rows ? launch_compress_rs<DT, 16, 2, 32, FP, 128>(a, ntiles, st)
                                  : launch_compress_rs<DT, PAMM_COMPRESS_RS32>(a, ntiles, st);
-        case 64: return few_rows ? launch_compress_rs<DT, 16, 2, 64, 4, 128>(a, ntiles, st)
+        case 64: return few_rows ? launch_compress_rs<DT, 16, 2, 64, FP, 128>(a, ntiles, st)
                                  : launch_compress_rs<DT, PAMM_COMPRESS_RS64>(a, ntiles, st);
         case 128: return launch_compress_rs<DT, PAMM_COMPRESS_RS128>(a, ntiles, st);
         default:
