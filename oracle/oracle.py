@@ -72,6 +72,19 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"oracle inputs are float32 or bf16-as-uint16, got {a.dtype}")
 
 
+def _rows_view(a: np.ndarray) -> tuple[np.ndarray, int]:
+    """(array, leading dimension in elements) for a row-major 2-D matrix.  A
+    view whose rows are contiguous but lie further apart than their length
+    (a column slice of a wider matrix) is passed as it is, with its row
+    stride as the leading dimension; anything else is copied densely."""
+    es = a.itemsize
+    if (a.ndim == 2 and a.shape[0] > 0 and a.shape[1] > 0 and a.strides[1] == es
+            and a.strides[0] % es == 0 and a.strides[0] // es >= a.shape[1]):
+        return a, a.strides[0] // es
+    a = np.ascontiguousarray(a)
+    return a, (a.shape[1] if a.ndim == 2 else 0)
+
+
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
@@ -91,11 +104,11 @@ def sample_generators(n: int, k: int, seed: int) -> np.ndarray:
 
 
 def gather(X: np.ndarray, gen_idx: np.ndarray) -> np.ndarray:
-    X = np.ascontiguousarray(X)
+    X, ldx = _rows_view(X)
     gen_idx = np.ascontiguousarray(gen_idx, dtype=np.int32)
     n, d = X.shape
     C = np.zeros((gen_idx.size, d), dtype=X.dtype)
-    _check(_load().orc_gather(_ptr(X), n, d, d, _dtype_code(X), _ptr(gen_idx), gen_idx.size, _ptr(C)), "gather")
+    _check(_load().orc_gather(_ptr(X), n, d, ldx, _dtype_code(X), _ptr(gen_idx), gen_idx.size, _ptr(C)), "gather")
     return C
 
 
@@ -103,8 +116,9 @@ def compress(X: np.ndarray, gen_idx: np.ndarray, eps: float, rows: np.ndarray | 
              want_scores: bool = False) -> dict:
     """Assign rows to generators.  Returns dict with C, f, alpha, cos, margin
     (and scores, nrows x k cosines, when ``want_scores``).  With ``rows`` only
-    those rows are processed; outputs follow the order of ``rows``."""
-    X = np.ascontiguousarray(X)
+    those rows are processed; outputs follow the order of ``rows``.  X may be
+    a view with contiguous rows and a larger row stride."""
+    X, ldx = _rows_view(X)
     gen_idx = np.ascontiguousarray(gen_idx, dtype=np.int32)
     n, d = X.shape
     k = gen_idx.size
@@ -118,7 +132,7 @@ def compress(X: np.ndarray, gen_idx: np.ndarray, eps: float, rows: np.ndarray | 
     cos = np.zeros(m, dtype=np.float64)
     margin = np.zeros(m, dtype=np.float64)
     scores = np.zeros((m, k), dtype=np.float64) if want_scores else None
-    rc = _load().orc_compress(_ptr(X), n, d, d, _dtype_code(X), _ptr(gen_idx), k, float(eps),
+    rc = _load().orc_compress(_ptr(X), n, d, ldx, _dtype_code(X), _ptr(gen_idx), k, float(eps),
                               _ptr(rows), m, _ptr(f), _ptr(alpha), _ptr(cos), _ptr(margin), _ptr(scores))
     _check(rc, "compress")
     out = {"C": gather(X, gen_idx), "f": f, "alpha": alpha, "cos": cos, "margin": margin}
@@ -129,9 +143,10 @@ def compress(X: np.ndarray, gen_idx: np.ndarray, eps: float, rows: np.ndarray | 
 
 def wgrad(C: np.ndarray, f: np.ndarray, alpha: np.ndarray, dY: np.ndarray,
           cols: np.ndarray | None = None) -> np.ndarray:
-    """Approximate weight gradient dW = C^T B~ (d x d_out, or d x len(cols)), fp64."""
+    """Approximate weight gradient dW = C^T B~ (d x d_out, or d x len(cols)), fp64.
+    dY may be a view with contiguous rows and a larger row stride."""
     C = np.ascontiguousarray(C)
-    dY = np.ascontiguousarray(dY)
+    dY, lddy = _rows_view(dY)
     if C.dtype != dY.dtype:
         raise TypeError("C and dY must share a dtype")
     f = np.ascontiguousarray(f, dtype=np.int32)
@@ -144,7 +159,7 @@ def wgrad(C: np.ndarray, f: np.ndarray, alpha: np.ndarray, dY: np.ndarray,
     else:
         nc = d_out
     dW = np.zeros((d, nc), dtype=np.float64)
-    rc = _load().orc_wgrad(_ptr(C), _dtype_code(C), _ptr(f), _ptr(alpha), n, k, d, _ptr(dY), d_out, d_out,
+    rc = _load().orc_wgrad(_ptr(C), _dtype_code(C), _ptr(f), _ptr(alpha), n, k, d, _ptr(dY), d_out, lddy,
                            _ptr(cols), nc, _ptr(dW))
     _check(rc, "wgrad")
     return dW

@@ -448,3 +448,107 @@ def test_clustered_inputs_assign_by_cluster():
     r = orc.compress(X, g, 0.5)
     assert (r["f"] >= 0).mean() > 0.9
     assert np.median(r["cos"]) > 0.95
+
+
+# --------------------------------------------------------------------------
+# decisions in fp32 (reading R8), NaN generators (R5), dropped rows in the
+# gradient, strided views, the rounding-band margin
+# --------------------------------------------------------------------------
+
+def test_argmax_decided_on_fp32_scores():
+    # Rows r0 = (1, 2^-12) and r1 = (1, 2^-13) are the generators; row r2 =
+    # (1, 0) scores 1/sqrt(1 + 2^-24) against r0 and 1/sqrt(1 + 2^-26)
+    # against r1.  The second is larger, but both lie within half an fp32
+    # ulp of 1 (1 - 2^-25 + O(2^-48) is just above the midpoint 1 - 2^-25,
+    # 1 - 2^-27 well above it), so both round to 1.0f: a tie, which the
+    # lowest slot wins.  An fp64 argmax would pick slot 1.
+    X = np.array([[1.0, 2.0 ** -12], [1.0, 2.0 ** -13], [1.0, 0.0]], dtype=np.float32)
+    r = orc.compress(X, np.array([0, 1]), 0.0)
+    assert r["f"][2] == 0
+    # alpha = fp32(1 / (1 + 2^-24)) = fp32(1 - 2^-24 + 2^-48) = 1 - 2^-24
+    assert r["alpha"][2] == np.float32(1.0 - 2.0 ** -24)
+    # the scores themselves still differ in fp64
+    s = orc.compress(X, np.array([0, 1]), 0.0, want_scores=True)["scores"][2]
+    assert s[1] > s[0] and np.float32(s[0]) == np.float32(s[1]) == np.float32(1.0)
+
+
+def test_eps_decided_on_fp32_cosine():
+    # Row (1, 0) against the single generator (1, 2^-12): cosine
+    # 1/sqrt(1 + 2^-24) < 1, which rounds to 1.0f.  With eps = 1 the fp32
+    # test keeps the row; an fp64 test would drop it.
+    X = np.array([[1.0, 2.0 ** -12], [1.0, 0.0]], dtype=np.float32)
+    r = orc.compress(X, np.array([0]), 1.0)
+    assert r["cos"][1] < 1.0
+    assert r["f"][1] == 0 and r["alpha"][1] == np.float32(1.0 - 2.0 ** -24)
+    # just above 1 nothing is kept
+    r = orc.compress(X, np.array([0]), float(np.nextafter(np.float32(1.0), np.float32(2.0))))
+    assert r["f"][1] == -1
+
+
+@pytest.mark.parametrize("bad", [np.inf, np.nan])
+def test_nonfinite_generator_never_wins(bad):
+    # A generator holding +inf scores NaN (inf / inf) against every row, and
+    # a NaN score never wins; one holding NaN has no usable norm and must
+    # not win either.  Checked with the bad generator in the first slot and
+    # in the last; the bad row itself is dropped (its cosine is NaN).
+    X = gauss(12, 5, 29)
+    X[2, 3] = bad
+    for g in (np.array([2, 6]), np.array([1, 2])):
+        r = orc.compress(X, g, 0.0)
+        bad_slot = int(np.nonzero(g == 2)[0][0])
+        other = [i for i in range(12) if i != 2]
+        assert np.all(r["f"][other] == 1 - bad_slot)
+        assert r["f"][2] == -1
+
+
+def test_wgrad_ignores_rows_outside_the_generators():
+    # f = -1 (dropped) and f >= k contribute nothing, whatever alpha says:
+    # dW equals that of the triple with those rows removed.
+    n, k, d, dout = 40, 5, 7, 6
+    rng = np.random.default_rng(31)
+    C = gauss(k, d, 32)
+    dY = gauss(n, dout, 33)
+    f = rng.integers(0, k, n).astype(np.int32)
+    alpha = rng.normal(size=n).astype(np.float32)
+    out = rng.random(n) < 0.4
+    f[out] = np.where(rng.random(out.sum()) < 0.5, -1, k)
+    full = orc.wgrad(C, f, alpha, dY)
+    kept = ~out
+    sub = orc.wgrad(C, f[kept], alpha[kept], dY[kept])
+    assert out.any() and kept.any()
+    assert np.array_equal(full, sub)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strided_views_match_dense_copies(dtype):
+    # X and dY as column slices of wider matrices whose extra columns hold
+    # NaN: any read past a row's d (or d_out) columns would poison the result.
+    n, d, dout, pad = 48, 10, 9, 6
+    X = gauss(n, d, 34, dtype)
+    dY = gauss(n, dout, 35, dtype)
+    nan = synth.f32_to_bf16_bits(np.float32(np.nan)) if dtype == "bf16" else np.float32(np.nan)
+    Xw = np.full((n, d + pad), nan, dtype=X.dtype)
+    Xw[:, :d] = X
+    dYw = np.full((n, dout + pad), nan, dtype=dY.dtype)
+    dYw[:, :dout] = dY
+    g = orc.sample_generators(n, 6, 36)
+    rv, rd = orc.compress(Xw[:, :d], g, 0.2), orc.compress(X, g, 0.2)
+    for key in ("C", "f", "alpha", "cos", "margin"):
+        assert np.array_equal(rv[key], rd[key]), key
+    assert np.array_equal(orc.wgrad(rd["C"], rd["f"], rd["alpha"], dYw[:, :dout]),
+                          orc.wgrad(rd["C"], rd["f"], rd["alpha"], dY))
+
+
+def test_margin_and_scores_closed_form():
+    # Generators e1 and e2; the row (3, 4) scores 3 and 4, cosine 4/5, and
+    # the gap to the runner-up is (4 - 3)/5.
+    X = np.array([[1.0, 0.0], [0.0, 1.0], [3.0, 4.0]], dtype=np.float32)
+    r = orc.compress(X, np.array([0, 1]), 0.0)
+    assert r["f"][2] == 1 and r["alpha"][2] == 4.0
+    assert abs(r["cos"][2] - 0.8) < 1e-15
+    assert abs(r["margin"][2] - 0.2) < 1e-15
+    # every generator's cosine: 3/5 and 4/5
+    sc = orc.compress(X, np.array([0, 1]), 0.0, want_scores=True)["scores"][2]
+    assert np.allclose(sc, [0.6, 0.8], rtol=0, atol=1e-15)
+    # a single generator has no runner-up
+    assert orc.compress(X, np.array([1]), 0.0)["margin"][2] == np.inf
