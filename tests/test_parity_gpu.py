@@ -262,6 +262,27 @@ def test_duplicate_generators_and_zero_and_nan_rows():
         check_wgrad(to_host(out["C"]), f_g, a_g, dY, to_host(out["dW"]))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_infinite_generator_never_wins(dtype):
+    # A generator holding +inf scores NaN (inf / inf) against every row, so it
+    # never wins; the row itself has a NaN cosine and is dropped.  Checked with
+    # that generator in the first slot and in a middle one (small-k kernel).
+    n, d = 300, 64
+    X32 = synth.random_matrix(n, d, 37, "f32").copy()
+    X32[150, 3] = np.inf
+    X = synth.f32_to_bf16_bits(X32) if dtype == "bf16" else X32
+    finite = np.arange(n) != 150
+    for g in (np.array([150, 160, 170, 180], dtype=np.int32), np.array([7, 150, 200, 250], dtype=np.int32)):
+        slot = int(np.nonzero(g == 150)[0][0])
+        for eps in (0.0, 0.2):
+            say("inf-generator", f"{dtype} slot={slot} eps={eps}")
+            out = run_gpu(X, None, g, eps)
+            f_g, a_g = to_host(out["f"]), to_host(out["alpha"])
+            assert f_g[150] == -1 and a_g[150] == 0.0
+            assert not np.any(f_g[finite] == slot)
+            check_compress(X, g, eps, to_host(out["C"]), f_g, a_g)
+
+
 @pytest.mark.parametrize("n,k", [
     (65536, 256),   # 256-row blocks, one generator tile: 4 waves of 128 x 128
     (32768, 256),   # 128-row blocks
@@ -270,7 +291,7 @@ def test_duplicate_generators_and_zero_and_nan_rows():
 def test_gemm_tiles_degenerate_rows(n, k):
     # the same degenerate cases on the GEMM-shaped kernel (bf16, 256-generator
     # tiles): duplicate and collinear generators, a zero generator, a zero
-    # row, a NaN row
+    # row, a NaN row, and a generator holding +inf
     d = 128
     X32 = synth.bf16_bits_to_f32(synth.random_matrix(n, d, 33, "bf16")).copy()
     X32[40] = X32[7]
@@ -278,11 +299,12 @@ def test_gemm_tiles_degenerate_rows(n, k):
     X32[100] = 0.0
     X32[101] = 0.0
     X32[102, 5] = np.nan
+    X32[150, 3] = np.inf    # a generator holding +inf: scores NaN, never wins
     X = synth.f32_to_bf16_bits(X32)
     rng = np.random.default_rng(34)
-    others = rng.choice(np.setdiff1d(np.arange(n), [7, 40, 41, 100, 101, 102, 200]), k - 4, replace=False)
-    g = np.sort(np.concatenate([[7, 40, 100, 200], others])).astype(np.int32)
-    s7, s100 = int(np.searchsorted(g, 7)), int(np.searchsorted(g, 100))
+    others = rng.choice(np.setdiff1d(np.arange(n), [7, 40, 41, 100, 101, 102, 150, 200]), k - 5, replace=False)
+    g = np.sort(np.concatenate([[7, 40, 100, 150, 200], others])).astype(np.int32)
+    s7, s100, s150 = (int(np.searchsorted(g, r)) for r in (7, 100, 150))
     gd = torch.from_numpy(g).cuda()
     for eps in (0.0, 0.2):
         say("gemm-degenerate", f"n={n} k={k} eps={eps}")
@@ -297,8 +319,9 @@ def test_gemm_tiles_degenerate_rows(n, k):
         else:
             assert f_g[101] == -1 and f_g[100] == -1
         nonzero = np.ones(n, bool)
-        nonzero[[100, 101, 102]] = False
+        nonzero[[100, 101, 102, 150]] = False
         assert not np.any(f_g[nonzero] == s100)   # the zero generator never wins a nonzero row
+        assert f_g[150] == -1 and not np.any(f_g == s150)
         check_compress(X, g, eps, to_host(C), f_g, a_g)
 
 
