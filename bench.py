@@ -297,7 +297,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle on the whole step", file=sys.stderr, flush=True)
         g0 = pamm.sample_generators(n, k, synth.generator_seed(name) + args.warmup).numpy()
         out["cpu_baseline"] = cpu_baseline(X, dY, g0, p, args.cpu_threads)
     print(json.dumps(out), flush=True)
