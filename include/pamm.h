@@ -57,7 +57,7 @@ typedef enum {
     PAMM_ERR_DTYPE = 3,       /* unknown dtype code                             */
     PAMM_ERR_ALIGN = 4,       /* pointer or leading dimension misaligned        */
     PAMM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
-    PAMM_ERR_UNSUPPORTED = 6, /* valid request this build does not implement    */
+    PAMM_ERR_UNSUPPORTED = 6, /* valid request the library does not implement   */
     PAMM_ERR_HIP = 7,         /* the HIP runtime reported an error at launch    */
     PAMM_ERR_VALUE = 8,       /* a scalar argument is out of range (e.g. eps)   */
     PAMM_ERR_TOO_LARGE = 9    /* needs more memory than available: the no-allocation

@@ -40,7 +40,7 @@ TIGHT = {"bf16": 1e-4, "f32": 1e-5}
 
 
 # host threads for the oracle: its C calls release the GIL, so row or column
-# chunks run in parallel (the GPU machines give one GPU a 16-core share)
+# chunks run in parallel on up to 16 host threads
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
