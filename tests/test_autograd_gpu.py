@@ -1,6 +1,7 @@
 """GPU: the transposed output of pamm_wgrad, and the PAMM linear layer's
 outputs and gradients against exact and oracle references."""
 import sys
+import warnings
 
 import numpy as np
 import pytest
@@ -103,6 +104,37 @@ def test_pamm_linear_with_every_row_a_generator_is_exact():
     torch.cuda.synchronize()
     exact = dY.double().cpu().T @ X.detach().double().cpu()
     assert rel(layer.weight.grad.double().cpu().numpy(), exact.numpy()) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pamm_linear_training_step_does_not_synchronize(dtype):
+    # Forward and backward enqueue work only: the generator draw goes to
+    # page-locked memory and uploads without a stream synchronisation, and no
+    # step reads a device value back.  torch's sync debug mode raises on any
+    # synchronising torch operation.
+    n, d, dout = 4096, 256, 384
+    say("PammLinear no sync", f"{dtype} n={n} d={d} d_out={dout}")
+    layer = PammLinear(d, dout, ratio=64, eps=0.1, device="cuda", dtype=dtype)
+    X = torch.randn(n, d, device="cuda", dtype=dtype, requires_grad=True)
+    dY = torch.randn(n, dout, device="cuda", dtype=dtype)
+    layer(X).backward(dY)                 # first call: library load, allocator warm-up
+    torch.cuda.synchronize()
+    layer.zero_grad(set_to_none=True)
+    X.grad = None
+    probe = torch.zeros(1, device="cuda")
+    prev = torch.cuda.get_sync_debug_mode()
+    with warnings.catch_warnings():   # torch warns that the mode is a prototype
+        warnings.simplefilter("ignore")
+        torch.cuda.set_sync_debug_mode("error")
+    try:
+        with pytest.raises(RuntimeError):
+            probe.item()                  # the mode is live: a read-back raises
+        for _ in range(2):
+            layer(X).backward(dY)
+    finally:
+        torch.cuda.set_sync_debug_mode(prev)
+    torch.cuda.synchronize()
+    assert torch.isfinite(layer.weight.grad.float()).all() and torch.isfinite(X.grad.float()).all()
 
 
 def test_error_sweep_runs_and_reports_sane_values():
